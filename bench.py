@@ -1,0 +1,178 @@
+#!/usr/bin/env python3
+"""Benchmark of the HGEMM hot path on one MI355X.
+
+A step is one C = A * Bt^T launch of the library's TN FP16 kernel at
+M = N = K = 8192 (FP16 inputs uniform in [-1, 1], FP32 accumulation, FP16
+output): the configuration whose throughput is quoted as a fraction of the
+MI355X dense FP16 matrix peak.  Inputs are seeded synthetic data, resident
+in HBM before the timed region starts.
+
+Prints one JSON line with TFLOPS (2*M*N*K / time), the roofline position of
+the kernel (HIP-event timing of every launch on the launch stream) and the
+CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 2516.6  # MI355X dense FP16/BF16 matrix peak: 256 CU x 4096 FLOP/clk x 2.4 GHz
+HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_hgemm_tn_f16_8192.json")
+KERNEL_SOURCES = ["device.hpp", "gemm_kernel.hpp", "hgemm_api.hip"]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for s in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dense_half_precision_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(kernel_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_digest") != kernel_source_digest() or t.get("kernel") != kernel_name:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, A, B, budget_s: float):
+    """The CPU oracle on a bounded band of full output rows of the workload."""
+    import oracle
+    oracle.build(0, force=False)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    band = 16
+    rows = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and rows < w.M:
+        r1 = min(w.M, rows + band)
+        oracle.hgemm(w.layout, w.dtype, A, B, rows=(rows, r1))
+        rows = r1
+        band = min(band * 2, 256)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"full output rows [0,{rows}) of {w.M} ({rows * w.N} of {w.M * w.N} "
+                      f"elements, FP64 accumulation) in {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=4, help="workload index 1..5 (default 4)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle sample budget (0 disables the cpu_baseline leg)")
+    ap.add_argument("--kernel", type=int, default=-1, help="kernel table index (-1 = automatic)")
+    ap.add_argument("--group-m", type=int, default=0)
+    ap.add_argument("--xcd-remap", type=int, default=-1)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this HGEMM runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(multi-GPU sharding is design-only, see the design notes)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from dense_half_precision_amd import hgemm, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 3
+    hgemm.lib()  # fail loudly if the HIP library is not built
+
+    w = inputs.workload(args.workload)
+    A, B = inputs.operands(w)
+    dev = torch.device("cuda:0")
+    dA = torch.from_numpy(A.view(np.int16)).to(dev)
+    dB = torch.from_numpy(B.view(np.int16)).to(dev)
+    dC = torch.empty((w.M, w.N), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    fn = hgemm.hgemm_tn_ex if w.layout == "tn" else hgemm.hgemm_nn_ex
+    kern = args.kernel if args.kernel >= 0 else hgemm.auto_kernel(
+        hgemm.TN if w.layout == "tn" else hgemm.NN, w.dtype, w.M, w.N, w.K)
+    kname = hgemm.kernel_table()[kern]["name"]
+
+    def launch():
+        st = fn(w.M, w.N, w.K, w.dtype, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), sp,
+                kernel=kern, group_m=args.group_m, xcd_remap=args.xcd_remap)
+        if st != hgemm.OK:
+            raise hgemm.HgemmError(st, "bench launch")
+
+    print(f"[bench] {w.describe()}; kernel {kname}; warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+
+    # timed region: events on the launch stream around every launch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
+    ms_step = wall * 1e3 / args.steps
+    value = w.flops / (ms_step * 1e-3) / 1e12
+    k_avg = float(per.mean())
+    achieved = w.flops / (k_avg * 1e-3) / 1e12
+    print(f"[bench] kernel ms: mean {k_avg:.4f} median {np.median(per):.4f} min {per.min():.4f} "
+          f"max {per.max():.4f}; wall ms/step {ms_step:.4f}", file=sys.stderr, flush=True)
+
+    tb = traffic_bytes(kname)
+    out = {
+        "metric": "HGEMM TFLOPS and % of MI355X dense FP16/BF16 MFMA peak at 4096³/8192³",
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "layout": w.layout, "M": w.M, "N": w.N, "K": w.K,
+                   "inputs": w.describe(), "kernel": kname, "accumulate": "fp32",
+                   "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": tb,
+                     "kernel_ms": {"mean": round(k_avg, 5), "median": round(float(np.median(per)), 5),
+                                   "min": round(float(per.min()), 5), "max": round(float(per.max()), 5)},
+                     "algorithmic_flops_per_launch": w.flops,
+                     "algorithmic_bytes_per_launch": w.algorithmic_bytes},
+    }
+    if args.cpu_seconds > 0:
+        print(f"[bench] cpu_baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
+              flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,222 @@
+"""Thin Python binding of libhgemm.so (the C ABI in include/hgemm.h).
+
+Only argument marshalling happens here; every step of the GEMM runs in the
+library's HIP kernels.  Importing this module does not need a GPU, but the
+library must be built (``__graft_entry__.build()``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB_PATH = os.path.join(PKG, "libhgemm.so")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("hgemm.h", "hgemm_probe.h")]
+
+F16, BF16 = 0, 1
+TN, NN = 0, 1
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+DTYPE_CODES = {"f16": F16, "fp16": F16, "float16": F16, "bf16": BF16, "bfloat16": BF16}
+LDS_XOR, LDS_PLAIN, LDS_PAD = 0, 1, 2
+
+
+class HgemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib().hgemm_status_string(status).decode()
+        if status == ERR_HIP:
+            msg += f" (hipError_t {_lib().hgemm_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("group_m", ctypes.c_int32),
+                ("xcd_remap", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_LIB = None
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    gemm = [i64, i64, i64, i32, vp, vp, vp, vp]
+    for name in ("hgemm_tn", "hgemm_nn"):
+        getattr(lib, name).argtypes = gemm
+        getattr(lib, name).restype = i32
+    for name in ("hgemm_tn_ex", "hgemm_nn_ex"):
+        getattr(lib, name).argtypes = gemm + [ctypes.POINTER(Config)]
+        getattr(lib, name).restype = i32
+    lib.hgemm_status_string.argtypes = [i32]
+    lib.hgemm_status_string.restype = ctypes.c_char_p
+    lib.hgemm_last_hip_error.restype = i32
+    lib.hgemm_version.restype = ctypes.c_char_p
+    lib.hgemm_kernel_count.restype = i32
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.hgemm_kernel_info.argtypes = [i32, ip, ip, ip, ip, ip]
+    lib.hgemm_kernel_info.restype = ctypes.c_char_p
+    lib.hgemm_auto_kernel.argtypes = [i32, i32, i64, i64, i64]
+    lib.hgemm_auto_kernel.restype = i32
+    lib.hgemm_probe_mfma.argtypes = [i32, vp, vp, vp, vp]
+    lib.hgemm_probe_mfma.restype = i32
+    lib.hgemm_probe_lds_roundtrip.argtypes = [i32, vp, vp, vp]
+    lib.hgemm_probe_lds_roundtrip.restype = i32
+    lib.hgemm_probe_tile_order.argtypes = [i32, i32, i32, i32, ip, ip]
+    lib.hgemm_probe_tile_order.restype = i32
+    _LIB = lib
+    return lib
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ctypes library (raises ImportError if it is not built)."""
+    return _lib()
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions declared in include/*.h."""
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"\b(hgemm_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def _dt(dtype) -> int:
+    return dtype if isinstance(dtype, int) else DTYPE_CODES[str(dtype).lower()]
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise HgemmError(status, where)
+
+
+# --- raw C-ABI calls (pointers as ints) --------------------------------------
+def hgemm_tn(M, N, K, dtype, A, Bt, C, stream=0) -> int:
+    return _lib().hgemm_tn(M, N, K, _dt(dtype), A, Bt, C, stream)
+
+
+def hgemm_nn(M, N, K, dtype, A, B, C, stream=0) -> int:
+    return _lib().hgemm_nn(M, N, K, _dt(dtype), A, B, C, stream)
+
+
+def hgemm_tn_ex(M, N, K, dtype, A, Bt, C, stream=0, kernel=-1, group_m=0, xcd_remap=-1) -> int:
+    cfg = Config(kernel, group_m, xcd_remap, 0)
+    return _lib().hgemm_tn_ex(M, N, K, _dt(dtype), A, Bt, C, stream, ctypes.byref(cfg))
+
+
+def hgemm_nn_ex(M, N, K, dtype, A, B, C, stream=0, kernel=-1, group_m=0, xcd_remap=-1) -> int:
+    cfg = Config(kernel, group_m, xcd_remap, 0)
+    return _lib().hgemm_nn_ex(M, N, K, _dt(dtype), A, B, C, stream, ctypes.byref(cfg))
+
+
+def kernel_table() -> list[dict]:
+    out = []
+    for i in range(_lib().hgemm_kernel_count()):
+        v = [ctypes.c_int() for _ in range(5)]
+        name = _lib().hgemm_kernel_info(i, *[ctypes.byref(x) for x in v])
+        out.append(dict(index=i, name=name.decode(), layout=v[0].value, dtype=v[1].value,
+                        bm=v[2].value, bn=v[3].value, bk=v[4].value))
+    return out
+
+
+def kernel_index(name: str) -> int:
+    for k in kernel_table():
+        if k["name"] == name:
+            return k["index"]
+    raise KeyError(name)
+
+
+def auto_kernel(layout, dtype, M, N, K) -> int:
+    return _lib().hgemm_auto_kernel(layout, _dt(dtype), M, N, K)
+
+
+# --- torch convenience (device memory and streams only) ----------------------
+def _torch_dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float16 or bfloat16")
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def matmul_tn(A, Bt, out=None, stream=None, **cfg):
+    """C = A @ Bt.T for CUDA tensors A[M,K], Bt[N,K] (row-major, same dtype)."""
+    import torch
+    if A.dim() != 2 or Bt.dim() != 2 or A.shape[1] != Bt.shape[1]:
+        raise ValueError(f"bad shapes {tuple(A.shape)} x {tuple(Bt.shape)}^T")
+    if A.dtype != Bt.dtype or not (A.is_cuda and Bt.is_cuda):
+        raise TypeError("A and Bt must be CUDA tensors of one dtype")
+    if not (A.is_contiguous() and Bt.is_contiguous()):
+        raise ValueError("A and Bt must be contiguous (row-major)")
+    M, K = A.shape
+    N = Bt.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    elif out.shape != (M, N) or out.dtype != A.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] tensor of the input dtype")
+    dt = _torch_dtype_code(A)
+    sp = _stream_ptr(stream)
+    if cfg:
+        st = hgemm_tn_ex(M, N, K, dt, A.data_ptr(), Bt.data_ptr(), out.data_ptr(), sp, **cfg)
+    else:
+        st = hgemm_tn(M, N, K, dt, A.data_ptr(), Bt.data_ptr(), out.data_ptr(), sp)
+    _check(st, "hgemm_tn")
+    return out
+
+
+def matmul_nn(A, B, out=None, stream=None, **cfg):
+    """C = A @ B for CUDA tensors A[M,K], B[K,N] (row-major, same dtype)."""
+    import torch
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"bad shapes {tuple(A.shape)} x {tuple(B.shape)}")
+    if A.dtype != B.dtype or not (A.is_cuda and B.is_cuda):
+        raise TypeError("A and B must be CUDA tensors of one dtype")
+    if not (A.is_contiguous() and B.is_contiguous()):
+        raise ValueError("A and B must be contiguous (row-major)")
+    M, K = A.shape
+    N = B.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    elif out.shape != (M, N) or out.dtype != A.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] tensor of the input dtype")
+    dt = _torch_dtype_code(A)
+    sp = _stream_ptr(stream)
+    if cfg:
+        st = hgemm_nn_ex(M, N, K, dt, A.data_ptr(), B.data_ptr(), out.data_ptr(), sp, **cfg)
+    else:
+        st = hgemm_nn(M, N, K, dt, A.data_ptr(), B.data_ptr(), out.data_ptr(), sp)
+    _check(st, "hgemm_nn")
+    return out
+
+
+def probe_mfma(dtype, x_ptr, y_ptr, d_ptr, stream=0) -> int:
+    return _lib().hgemm_probe_mfma(_dt(dtype), x_ptr, y_ptr, d_ptr, stream)
+
+
+def probe_lds_roundtrip(lds_layout, src_ptr, dst_ptr, stream=0) -> int:
+    return _lib().hgemm_probe_lds_roundtrip(lds_layout, src_ptr, dst_ptr, stream)
+
+
+def tile_order(tiles_m, tiles_n, group_m, xcd_remap):
+    """(tm, tn) lists: the tile each workgroup id computes (host-side code)."""
+    total = tiles_m * tiles_n
+    tm = (ctypes.c_int * total)()
+    tn = (ctypes.c_int * total)()
+    _check(_lib().hgemm_probe_tile_order(tiles_m, tiles_n, group_m, xcd_remap, tm, tn),
+           "hgemm_probe_tile_order")
+    return list(tm), list(tn)

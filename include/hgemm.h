@@ -1,0 +1,132 @@
+/*
+ * hgemm.h -- C ABI of libhgemm.so: dense half-precision GEMM on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Operation (the naive matmul of the "tcgen05 for dummies" translation,
+ * "[译] tcgen05 入门：从零实现 B200 GEMM", section "Recap: how to write a
+ * high-performance matmul kernel"; the TN/NN layouts of the kernel header in
+ * "HGEMM: WMMA 与 MMA PTX 代码学习", full-listing section):
+ *
+ *     C[m][n] = round_to_dtype( sum_{k<K} A[m][k] * Bop[k][n] )
+ *
+ * with FP16 or BF16 inputs, products and sums carried in FP32 by the matrix
+ * cores (the FP32-accumulate-then-convert outline of section 3 of
+ * "MTT S4000 张量核心 GEMM 优化…"), and one round-to-nearest-even conversion
+ * of each FP32 sum to the output type.  C is overwritten (never read): there
+ * is no alpha/beta.
+ *
+ * Layouts (all dense, packed, row-major, element size 2 bytes):
+ *   TN: A is M x K (lda = K); B is stored as Bt, N x K (ldb = K), so
+ *       Bop[k][n] = Bt[n][k]; C is M x N (ldc = N).
+ *   NN: A is M x K (lda = K); B is K x N (ldb = N); C is M x N (ldc = N).
+ *
+ * Accepted shapes: M, N, K >= 0; N % 8 == 0 and K % 8 == 0 so that every row
+ * of every operand starts on a 16-byte boundary; M <= 2^30, N <= 2^23,
+ * K <= 2^21, and the grid of output tiles below 2^31 workgroups (these keep
+ * every per-tile byte offset in 32 bits).  M and N need not be multiples of any tile:
+ * edge tiles are predicated.  M == 0 or N == 0 is a no-op; K == 0 writes
+ * +0 to all of C (the empty sum).
+ *
+ * Pointers: A, B and C are device pointers on the current HIP device, each
+ * 16-byte aligned, owned and allocated by the caller.  A and B are read-only
+ * here; C must not overlap A or B.  The library allocates nothing and keeps
+ * no pointer after a call returns.
+ *
+ * Streams: `stream` is a hipStream_t (NULL = the default stream).  Every call
+ * only enqueues work on that stream and returns without synchronising; the
+ * caller orders and waits with events or stream syncs.  Calls are re-entrant
+ * and thread-safe.
+ *
+ * Errors: every entry point returns an hgemm_status_t and never prints or
+ * throws.  Arguments are validated before anything is launched, so a non-OK
+ * status other than HGEMM_ERR_HIP means nothing was enqueued.
+ */
+#ifndef HGEMM_H
+#define HGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hgemm_dtype {
+  HGEMM_F16 = 0,  /* IEEE binary16 inputs and output */
+  HGEMM_BF16 = 1  /* bfloat16 inputs and output */
+} hgemm_dtype_t;
+
+typedef enum hgemm_status {
+  HGEMM_OK = 0,
+  HGEMM_ERR_INVALID_ARG = 1, /* negative dimension, unknown dtype, NULL
+                                pointer while M*N > 0 (or M*N*K > 0 for
+                                A and B), bad config */
+  HGEMM_ERR_UNSUPPORTED = 2, /* N or K not a multiple of 8, a pointer not
+                                16-byte aligned, a dimension over the limits
+                                above, or a config that does not fit */
+  HGEMM_ERR_HIP = 3          /* the HIP runtime refused a launch; the
+                                hipError_t is kept per thread, see
+                                hgemm_last_hip_error() */
+} hgemm_status_t;
+
+/* C[M,N] = A[M,K] * Bt[N,K]^T.  A, Bt, C as described above. */
+hgemm_status_t hgemm_tn(int64_t M, int64_t N, int64_t K, int dtype,
+                        const void *A, const void *Bt, void *C, void *stream);
+
+/* C[M,N] = A[M,K] * B[K,N].  A, B, C as described above. */
+hgemm_status_t hgemm_nn(int64_t M, int64_t N, int64_t K, int dtype,
+                        const void *A, const void *B, void *C, void *stream);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char *hgemm_status_string(int status);
+
+/* hipError_t of this thread's last HGEMM_ERR_HIP (0 if none yet). */
+int hgemm_last_hip_error(void);
+
+/* Library version string, e.g. "hgemm-gfx950 1.0". */
+const char *hgemm_version(void);
+
+/*
+ * Explicit kernel selection, for tuning and for the ablations that back each
+ * design choice with counters (tile shape, LDS layout, block-index swizzle).
+ * The pages' launchers expose the same kind of knobs at run time (stages,
+ * block swizzle on/off and its stride) in the torch bindings of the HGEMM
+ * MMA note and the CuTe note.
+ */
+typedef struct hgemm_config {
+  int32_t kernel;    /* index into the kernel table, or -1 for the automatic
+                        choice; the entry's layout and dtype must match the
+                        call */
+  int32_t group_m;   /* tile rows per group of the grouped block order
+                        (>= 1), or 0 for the kernel's default */
+  int32_t xcd_remap; /* 1: give each XCD a contiguous range of tiles;
+                        0: plain dispatch order; -1: default (on) */
+  int32_t reserved;  /* must be 0 */
+} hgemm_config_t;
+
+/* As hgemm_tn / hgemm_nn, with an explicit configuration (NULL = automatic). */
+hgemm_status_t hgemm_tn_ex(int64_t M, int64_t N, int64_t K, int dtype,
+                           const void *A, const void *Bt, void *C, void *stream,
+                           const hgemm_config_t *cfg);
+hgemm_status_t hgemm_nn_ex(int64_t M, int64_t N, int64_t K, int dtype,
+                           const void *A, const void *B, void *C, void *stream,
+                           const hgemm_config_t *cfg);
+
+/* Number of entries in the kernel table. */
+int hgemm_kernel_count(void);
+
+/* Description of kernel table entry `index` (NULL if out of range):
+ * "<layout>_<dtype>_<BM>x<BN>x<BK>_<lds layout>".  The integers describing it
+ * are written through the non-NULL pointers: layout 0 = TN, 1 = NN; dtype as
+ * hgemm_dtype_t; the workgroup tile BM x BN x BK. */
+const char *hgemm_kernel_info(int index, int *layout, int *dtype, int *bm,
+                              int *bn, int *bk);
+
+/* Kernel table index the automatic choice would use for this call (layout
+ * 0 = TN, 1 = NN), or -1 for invalid arguments. */
+int hgemm_auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HGEMM_H */

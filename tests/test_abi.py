@@ -1,0 +1,116 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+declared symbol, and rejects bad arguments with the documented codes before
+launching anything."""
+import ctypes
+
+import pytest
+
+from dense_half_precision_amd import hgemm
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return hgemm.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = hgemm.declared_functions()
+    assert {"hgemm_tn", "hgemm_nn", "hgemm_tn_ex", "hgemm_nn_ex"} <= set(names)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, f"declared but not exported: {missing}"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.hgemm_version().decode().startswith("hgemm-gfx950")
+    for code, text in ((0, "ok"), (1, "invalid argument"), (3, "HIP runtime error")):
+        assert lib.hgemm_status_string(code).decode() == text
+    assert lib.hgemm_status_string(99).decode() == "unknown status"
+    assert lib.hgemm_last_hip_error() == 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails or the call is a no-op
+
+
+@pytest.mark.parametrize("fn", [hgemm.hgemm_tn, hgemm.hgemm_nn])
+def test_validation_codes(fn):
+    inv, uns = hgemm.ERR_INVALID_ARG, hgemm.ERR_UNSUPPORTED
+    assert fn(-1, 8, 8, 0, FAKE, FAKE, FAKE) == inv
+    assert fn(8, -8, 8, 0, FAKE, FAKE, FAKE) == inv
+    assert fn(8, 8, -8, 0, FAKE, FAKE, FAKE) == inv
+    assert fn(8, 8, 8, 7, FAKE, FAKE, FAKE) == inv          # unknown dtype
+    assert fn(8, 8, 8, 0, FAKE, FAKE, 0) == inv             # NULL C
+    assert fn(8, 8, 8, 0, 0, FAKE, FAKE) == inv             # NULL A
+    assert fn(8, 8, 8, 1, FAKE, 0, FAKE) == inv             # NULL B
+    assert fn(8, 12, 8, 0, FAKE, FAKE, FAKE) == uns         # N % 8
+    assert fn(8, 8, 12, 0, FAKE, FAKE, FAKE) == uns         # K % 8
+    assert fn(8, 8, 8, 0, FAKE + 2, FAKE, FAKE) == uns      # misaligned A
+    assert fn(8, 8, 8, 0, FAKE, FAKE + 8, FAKE) == uns      # misaligned B
+    assert fn(8, 8, 8, 0, FAKE, FAKE, FAKE + 4) == uns      # misaligned C
+    assert fn((1 << 30) + 1, 8, 8, 0, FAKE, FAKE, FAKE) == uns
+    assert fn(8, (1 << 23) + 8, 8, 0, FAKE, FAKE, FAKE) == uns
+    assert fn(8, 8, (1 << 21) + 8, 0, FAKE, FAKE, FAKE) == uns
+    # empty outputs are no-ops and launch nothing, even with NULL pointers
+    assert fn(0, 8, 8, 0, 0, 0, 0) == hgemm.OK
+    assert fn(8, 0, 8, 1, 0, 0, 0) == hgemm.OK
+
+
+def test_ex_config_validation():
+    inv = hgemm.ERR_INVALID_ARG
+    tab = hgemm.kernel_table()
+    tn16 = next(k["index"] for k in tab if k["layout"] == hgemm.TN and k["dtype"] == hgemm.F16)
+    nn16 = next(k["index"] for k in tab if k["layout"] == hgemm.NN and k["dtype"] == hgemm.F16)
+    assert hgemm.hgemm_tn_ex(8, 8, 8, 0, FAKE, FAKE, FAKE, kernel=nn16) == inv  # wrong layout
+    assert hgemm.hgemm_tn_ex(8, 8, 8, 1, FAKE, FAKE, FAKE, kernel=tn16) == inv  # wrong dtype
+    assert hgemm.hgemm_tn_ex(8, 8, 8, 0, FAKE, FAKE, FAKE, kernel=len(tab)) == inv
+    assert hgemm.hgemm_tn_ex(8, 8, 8, 0, FAKE, FAKE, FAKE, group_m=-1) == inv
+    assert hgemm.hgemm_tn_ex(8, 8, 8, 0, FAKE, FAKE, FAKE, xcd_remap=2) == inv
+    cfg = hgemm.Config(-1, 0, -1, 5)  # reserved must be 0
+    st = hgemm.lib().hgemm_tn_ex(8, 8, 8, 0, FAKE, FAKE, FAKE, 0, ctypes.byref(cfg))
+    assert st == inv
+
+
+def test_kernel_table_and_auto_choice():
+    tab = hgemm.kernel_table()
+    assert len(tab) == hgemm.lib().hgemm_kernel_count() > 0
+    assert hgemm.lib().hgemm_kernel_info(len(tab), None, None, None, None, None) is None
+    for k in tab:
+        assert k["layout"] in (0, 1) and k["dtype"] in (0, 1) and k["bk"] == 64
+        lay = "tn" if k["layout"] == 0 else "nn"
+        assert k["name"].startswith(f"{lay}_{'f16' if k['dtype'] == 0 else 'bf16'}_")
+    # every layout/dtype has an automatic choice, matching layout and dtype
+    for lay in (0, 1):
+        for dt in (0, 1):
+            for M, N in ((1, 8), (512, 512), (2048, 2048), (8192, 8192)):
+                i = hgemm.auto_kernel(lay, dt, M, N, 64)
+                assert 0 <= i < len(tab)
+                assert tab[i]["layout"] == lay and tab[i]["dtype"] == dt
+    assert hgemm.auto_kernel(2, 0, 8, 8, 8) == -1
+    assert hgemm.auto_kernel(0, 0, 0, 8, 8) == -1
+    # the large configurations get the 256 x 256 tile, the square 2048 the 128 one
+    assert tab[hgemm.auto_kernel(0, 0, 8192, 8192, 8192)]["bm"] == 256
+    assert tab[hgemm.auto_kernel(1, 1, 4096, 4096, 4096)]["bm"] == 256
+    assert tab[hgemm.auto_kernel(0, 0, 2048, 2048, 2048)]["bm"] == 128
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n", [(1, 1), (2, 2), (3, 5), (32, 32), (16, 16), (8, 8),
+                                              (5, 33), (33, 7), (4, 64), (128, 2)])
+@pytest.mark.parametrize("group_m", [1, 3, 8, 16])
+@pytest.mark.parametrize("xcd", [0, 1])
+def test_tile_order_is_a_bijection(tiles_m, tiles_n, group_m, xcd):
+    """Every workgroup computes a distinct in-range tile and every tile is
+    computed (the kernels' own mapping, run on the host)."""
+    tm, tn = hgemm.tile_order(tiles_m, tiles_n, group_m, xcd)
+    assert all(0 <= a < tiles_m for a in tm) and all(0 <= b < tiles_n for b in tn)
+    assert len(set(zip(tm, tn))) == tiles_m * tiles_n
+
+
+def test_tile_order_locality():
+    """With the XCD remap, the 32 workgroups an XCD runs at once (ids x, x+8,
+    x+16, ...) cover a compact block of tiles: at most 8 tile rows and 4 tile
+    columns for an 8192^2 output of 256^2 tiles and group_m = 8."""
+    tm, tn = hgemm.tile_order(32, 32, 8, 1)
+    for x in range(8):
+        ids = [x + 8 * j for j in range(32)]
+        rows = {tm[i] for i in ids}
+        cols = {tn[i] for i in ids}
+        assert len(rows) <= 8 and len(cols) <= 4, (x, sorted(rows), sorted(cols))

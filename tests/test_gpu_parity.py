@@ -1,0 +1,159 @@
+"""Parity of the HIP path with the CPU oracle (GPU).
+
+* The five measured workloads at full size, in the launch configuration the
+  bench times (automatic kernel choice): full output for the 512^3 and 2048^3
+  cases; for the larger ones a stratified seeded sample of 4096 elements (one
+  per cell of a 64 x 64 grid over C) plus a whole-output Freivalds projection.
+* Ragged and degenerate shapes, every kernel of the table, exact integer
+  cases, layout invariants and run-to-run determinism.
+"""
+import numpy as np
+import pytest
+
+import helpers
+import oracle
+from dense_half_precision_amd import hgemm, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _oracle_built():
+    oracle.build(0, force=False)
+
+
+# ------------------------------------------------------------ full workloads
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_workload_parity(idx):
+    w = inputs.workload(idx)
+    print(f"\n[parity] workload {idx}: {w.describe()}", flush=True)
+    A, B = inputs.operands(w)
+    C = helpers.gpu_gemm(w.layout, w.dtype, A, B)
+    if w.M * w.N * w.K <= 2048 ** 3:
+        ref = oracle.hgemm(w.layout, w.dtype, A, B)
+        stats = helpers.parity(C, ref, w.dtype, w.name)
+    else:
+        rows, cols = inputs.stratified_samples(w.M, w.N, inputs.SAMPLE_SEED_BASE + idx)
+        ref = oracle.hgemm_sampled(w.layout, w.dtype, A, B, rows, cols)
+        stats = helpers.parity(C[rows, cols], ref, w.dtype, w.name)
+        helpers.freivalds(C, A, B, w.layout, w.dtype)
+    print(f"[parity] workload {idx}: {stats}", flush=True)
+
+
+# ------------------------------------------------------------ ragged / edges
+EDGE_SHAPES = [
+    (1, 8, 8), (17, 24, 72), (300, 136, 200), (257, 264, 64), (64, 64, 8),
+    (255, 248, 520), (129, 1000, 200), (1000, 1000, 72), (513, 520, 136),
+]
+
+
+@pytest.mark.parametrize("layout", ["tn", "nn"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_edge_shapes_auto(layout, dtype):
+    w = inputs.Workload(0, layout, dtype, 0, 0, 0, "uniform")
+    for s, (M, N, K) in enumerate(EDGE_SHAPES):
+        A, B = inputs.operands(w, M, N, K, seed_offset=10 * s)
+        C = helpers.gpu_gemm(layout, dtype, A, B)
+        helpers.parity(C, oracle.hgemm(layout, dtype, A, B), dtype, f"{layout} {dtype} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("kernel", range(16))
+def test_every_kernel_ragged(kernel):
+    tab = hgemm.kernel_table()
+    if kernel >= len(tab):
+        pytest.skip("no such kernel")
+    k = tab[kernel]
+    layout = "tn" if k["layout"] == hgemm.TN else "nn"
+    dtype = "f16" if k["dtype"] == hgemm.F16 else "bf16"
+    w = inputs.Workload(0, layout, dtype, 0, 0, 0, "normal")
+    # two tile rows/cols plus a ragged edge, and a K tail
+    M, N, K = 2 * k["bm"] + 5, 2 * k["bn"] + 24, 3 * k["bk"] + 40
+    A, B = inputs.operands(w, M, N, K, seed_offset=kernel)
+    for gm, xcd in ((0, -1), (1, 0), (3, 1)):
+        C = helpers.gpu_gemm(layout, dtype, A, B, kernel=kernel, group_m=gm, xcd_remap=xcd)
+        helpers.parity(C, oracle.hgemm(layout, dtype, A, B), dtype, f"{k['name']} gm={gm} xcd={xcd}")
+
+
+@pytest.mark.parametrize("layout", ["tn", "nn"])
+def test_k_zero_writes_zeros(layout):
+    M, N = 40, 48
+    A = np.zeros((M, 0), dtype=np.uint16)
+    B = np.zeros((N, 0) if layout == "tn" else (0, N), dtype=np.uint16)
+    import torch
+    dA = torch.zeros(8, dtype=torch.int16, device="cuda")  # K = 0: never read
+    C = helpers.gpu_gemm(layout, "f16", A, B, dA=dA, dB=dA)
+    assert np.all(C == 0)
+
+
+def test_empty_outputs_are_noops():
+    out = helpers.empty_dev(4, 8, fill=0x1234)
+    st = hgemm.hgemm_tn(0, 8, 16, "f16", 0, 0, out.data_ptr(), helpers.stream_ptr())
+    assert st == hgemm.OK
+    assert np.all(helpers.to_host(out) == 0x1234)
+
+
+@pytest.mark.parametrize("layout", ["tn", "nn"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_small_integers_exact(layout, dtype):
+    """Products and sums exact in FP32 and in the output type: C must equal
+    the int64 matmul bit for bit (f16: |x| <= 2, K <= 512; bf16: |x| <= 1,
+    K <= 256)."""
+    g = np.random.Generator(np.random.PCG64(21))
+    hi, K = (2, 512) if dtype == "f16" else (1, 256)
+    for M, N in ((300, 264), (64, 1000)):
+        Ai = g.integers(-hi, hi + 1, size=(M, K))
+        Bi = g.integers(-hi, hi + 1, size=(K, N))
+        to = (lambda v: v.astype(np.float16).view(np.uint16)) if dtype == "f16" else \
+            (lambda v: inputs.f32_to_bf16_bits(v.astype(np.float32)))
+        Bst = Bi.T.copy() if layout == "tn" else Bi
+        C = helpers.gpu_gemm(layout, dtype, to(Ai), to(Bst))
+        assert np.array_equal(C, to(Ai @ Bi))
+
+
+def test_identity_and_permutation_exact():
+    g = np.random.Generator(np.random.PCG64(22))
+    K, N = 264, 136
+    Bop = inputs.draw((K, N), "f16", "normal", 5)
+    for layout in ("tn", "nn"):
+        Bst = Bop.T.copy() if layout == "tn" else Bop
+        eye = np.eye(K).astype(np.float16).view(np.uint16)
+        assert np.array_equal(helpers.gpu_gemm(layout, "f16", eye, Bst), Bop)
+        perm = g.permutation(K)
+        P = np.zeros((K, K))
+        P[np.arange(K), perm] = 1.0
+        assert np.array_equal(helpers.gpu_gemm(layout, "f16", P.astype(np.float16).view(np.uint16),
+                                               Bst), Bop[perm])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_layout_invariants(dtype):
+    """TN(A, Bt) == NN(A, Bt^T) and TN(A, Bt)^T == TN(Bt, A) within parity;
+    the TN/NN pair shares the inner loop, so it is also bit-identical."""
+    M, N, K = 392, 520, 328
+    A = inputs.draw((M, K), dtype, "uniform", 61)
+    Bt = inputs.draw((N, K), dtype, "uniform", 62)
+    tn = helpers.gpu_gemm("tn", dtype, A, Bt)
+    nn = helpers.gpu_gemm("nn", dtype, A, Bt.T.copy())
+    assert np.array_equal(tn, nn)
+    tr = helpers.gpu_gemm("tn", dtype, Bt, A)
+    helpers.parity(tn.T, tr, dtype, "transpose")
+
+
+def test_determinism_and_streams():
+    """Same inputs give bit-identical C across repeats, launch orders and
+    streams (no atomics, no split-K): a tripwire for races."""
+    import torch
+    w = inputs.workload(3)
+    A, B = inputs.operands(w, 2048, 2048, 1024)
+    dA, dB = helpers.to_dev(A), helpers.to_dev(B)
+    first = helpers.gpu_gemm("nn", "bf16", A, B, dA=dA, dB=dB)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = [helpers.empty_dev(2048, 2048) for _ in range(4)]
+    for i, o in enumerate(outs):
+        s = s1 if i % 2 == 0 else s2
+        st = hgemm.hgemm_nn(2048, 2048, 1024, "bf16", dA.data_ptr(), dB.data_ptr(), o.data_ptr(),
+                            s.cuda_stream)
+        assert st == hgemm.OK
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(helpers.to_host(o), first)

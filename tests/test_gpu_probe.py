@@ -1,0 +1,71 @@
+"""GPU unit tests of the building blocks the kernels rest on: the MFMA
+operand/accumulator lane map and the LDS store/read addressing."""
+import numpy as np
+import pytest
+
+import helpers
+from dense_half_precision_amd import hgemm, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(vals, dtype):
+    v = np.asarray(vals, dtype=np.float64)
+    if dtype == "f16":
+        return v.astype(np.float16).view(np.uint16)
+    return inputs.f32_to_bf16_bits(v.astype(np.float32))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_mfma_lane_map(dtype):
+    """Lane l holds X[l%32][8*(l//32)+e] and Y[8*(l//32)+e][l%32]; accumulator
+    r of lane l is D[8*(r//4) + 4*(l//32) + r%4][l%32].  Small integers keep
+    every product and sum exact, so the comparison is bit-exact."""
+    import torch
+    g = np.random.Generator(np.random.PCG64(3))
+    X = g.integers(-3, 4, size=(32, 16))
+    Y = g.integers(-3, 4, size=(16, 32))
+    D = X @ Y
+    lane = np.arange(64)
+    e = np.arange(8)
+    xl = X[(lane % 32)[:, None], (8 * (lane // 32))[:, None] + e[None, :]]
+    yl = Y[(8 * (lane // 32))[:, None] + e[None, :], (lane % 32)[:, None]]
+    dx, dy = helpers.to_dev(_bits(xl, dtype)), helpers.to_dev(_bits(yl, dtype))
+    dd = torch.full((64, 16), float("nan"), dtype=torch.float32, device="cuda")
+    st = hgemm.probe_mfma(dtype, dx.data_ptr(), dy.data_ptr(), dd.data_ptr(), helpers.stream_ptr())
+    assert st == hgemm.OK
+    got = dd.cpu().numpy()
+    r = np.arange(16)
+    want = D[8 * (r[None, :] // 4) + 4 * (lane[:, None] // 32) + r[None, :] % 4, (lane % 32)[:, None]]
+    assert np.array_equal(got, want.astype(np.float32))
+
+
+def test_mfma_k_order_is_shared():
+    """Only the pairing of X and Y elements along k matters to a GEMM: a
+    one-hot k in X must meet the same k in Y (probe each of the 16 k)."""
+    import torch
+    for k in range(16):
+        X = np.zeros((32, 16))
+        Y = np.zeros((16, 32))
+        X[:, k] = 1.0
+        Y[k, :] = 2.0
+        lane = np.arange(64)
+        e = np.arange(8)
+        xl = X[(lane % 32)[:, None], (8 * (lane // 32))[:, None] + e[None, :]]
+        yl = Y[(8 * (lane // 32))[:, None] + e[None, :], (lane % 32)[:, None]]
+        dx, dy = helpers.to_dev(_bits(xl, "f16")), helpers.to_dev(_bits(yl, "f16"))
+        dd = torch.zeros((64, 16), dtype=torch.float32, device="cuda")
+        assert hgemm.probe_mfma("f16", dx.data_ptr(), dy.data_ptr(), dd.data_ptr(),
+                                helpers.stream_ptr()) == hgemm.OK
+        assert np.all(dd.cpu().numpy() == 2.0), f"k={k}"
+
+
+@pytest.mark.parametrize("layout", [hgemm.LDS_XOR, hgemm.LDS_PLAIN, hgemm.LDS_PAD])
+def test_lds_roundtrip(layout):
+    import torch
+    src = np.random.Generator(np.random.PCG64(4)).integers(0, 65536, size=(256, 64)).astype(np.uint16)
+    ds = helpers.to_dev(src)
+    dd = torch.zeros((256, 64), dtype=torch.int16, device="cuda")
+    assert hgemm.probe_lds_roundtrip(layout, ds.data_ptr(), dd.data_ptr(),
+                                     helpers.stream_ptr()) == hgemm.OK
+    assert np.array_equal(helpers.to_host(dd), src)
