@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = 2516.6  # MI355X dense FP16/BF16 matrix peak: 256 CU x 4096 FLOP/clk x 2.4 GHz
 HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_hgemm_tn_f16_8192.json")
-KERNEL_SOURCES = ["device.hpp", "gemm_kernel.hpp", "hgemm_api.hip"]
+KERNEL_SOURCES = ["device.hpp", "common.hpp", "gemm_kernel.hpp", "gemm_regstage.hpp", "hgemm_api.hip"]
 
 
 def kernel_source_digest() -> str:
@@ -81,6 +81,9 @@ def main() -> int:
     ap.add_argument("--kernel", type=int, default=-1, help="kernel table index (-1 = automatic)")
     ap.add_argument("--group-m", type=int, default=0)
     ap.add_argument("--xcd-remap", type=int, default=-1)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the GEMM, run a plain device copy of this many MiB "
+                         "(reference point for scaling FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -96,6 +99,16 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 3
     hgemm.lib()  # fail loudly if the HIP library is not built
+
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": args.warmup + args.steps}), flush=True)
+        return 0
 
     w = inputs.workload(args.workload)
     A, B = inputs.operands(w)

@@ -33,6 +33,34 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 x, u32x4 y, f32x16 c) {
   }
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// 16x16x32 MFMA, FP32 accumulate: D[i][j] = sum_k X[i][k] * Y[k][j] + Cin.
+// Lane l holds 8 consecutive-k elements of X (row i = l % 16) and of Y
+// (column j = l % 16), lane group l / 16 holding k = 8*(l/16) .. +7; lane l,
+// accumulator r holds D[4*(l/16) + r][l % 16].
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 x, u32x4 y, f32x4 c) {
+  if constexpr (DT == kF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x),
+                                                  __builtin_bit_cast(f16x8, y), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
+                                                   __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
+  }
+}
+
+// Transposing LDS read of 16-bit data (ds_read_b64_tr_b16).  Within each group
+// of 16 lanes, lane i points at 4 consecutive elements; lane l receives element
+// (l % 4) of the row that lane 4*j + l/4 points at, for j = 0..3.  Addresses
+// are byte offsets into the workgroup's LDS, 8-byte aligned.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void *lds_ptr) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4 *)(lds_ptr));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Two FP32 values -> packed pair of 16-bit values, round to nearest even
 // (the default round mode of the FP32 -> FP16 and FP32 -> BF16 converts).
 template <int DT>
@@ -60,6 +88,33 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0);
+}
+
+// 16-byte buffer load of every lane straight into LDS: lane l's data lands at
+// lds_base + 16*l (lds_base must be the same for the whole wave);
+// out-of-range offsets read zero.
+__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                           void *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void *)lds_base, 16, voffset, 0, 0, 0);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): the caller
+// waits (s_waitcnt) for exactly the LDS reads/writes other waves depend on.
+// __syncthreads() would also drain every outstanding direct-to-LDS load
+// (it counts as a pending LDS write), which would serialise the pipeline.
+// The empty asm statements keep the compiler from moving memory operations
+// across the barrier.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most vm outstanding
+// vector-memory operations and at most lgkm LDS/scalar operations remain.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 0xF) | (((vm >> 4) & 0x3) << 14) | (0x7 << 4) | ((lgkm & 0xF) << 8);
 }
 
 }  // namespace hgemm

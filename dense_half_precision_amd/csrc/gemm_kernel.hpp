@@ -1,278 +1,338 @@
-// gemm_kernel.hpp -- the HGEMM kernel template for gfx950.
+// gemm_kernel.hpp -- the HGEMM kernel for gfx950.
 //
-// One workgroup computes a BM x BN tile of C with four 64-wide waves, each
-// owning a (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA blocks whose FP32
-// accumulators stay in registers for the whole K loop (the output-stationary
-// tiling of the tcgen05 translation's "tiled_matmul" recap; the block -> warp
-// -> MMA hierarchy of the HGEMM MMA note, section on the fractal structure;
-// the S4000 post's section 3.1 on block and warp tiling).
+// One workgroup of four 64-wide waves (2 x 2) computes a BM x BN tile of C;
+// each wave owns a (BM/2) x (BN/2) block made of 16x16 MFMA tiles whose FP32
+// accumulators stay in registers for the whole K loop: the output-stationary
+// tiling of the tcgen05 translation's tiled_matmul recap and the block ->
+// warp -> MMA hierarchy of the HGEMM MMA note (fractal-structure section) and
+// of section 3.1 of the S4000 post.
 //
-// Per K step of BK = 64:
-//   global -> registers : 16-byte buffer loads, 8 lanes per 128-byte row, so
-//                         each wave reads whole cache lines (S4000 post 3.2,
-//                         vectorised loads); rows past M/N and k past K read
-//                         as zero through the buffer range check.
-//   registers -> LDS    : 16-byte stores into a 2-stage ring (the multi-stage
-//                         pipeline of the HGEMM MMA note and the tcgen05
-//                         translation's pipelining section).  Each 128-byte
-//                         row of 8 chunks is stored with chunk c at position
-//                         c ^ (row & 7), an XOR swizzle in the spirit of the
-//                         CuTe note's Swizzle<3,3,3> and the ablation draft's
-//                         section 3 bank analysis, re-derived for the 16-byte
-//                         LDS reads below.
-//   LDS -> registers    : one 16-byte read per operand fragment and lane
-//                         (8 consecutive k of one row).
-//   MFMA                : v_mfma_f32_32x32x16_{f16,bf16}.
-// The operands are fed swapped (B tile as the MFMA's first operand), so each
-// lane ends up holding four consecutive columns of one row of C, which the
-// epilogue converts to FP16/BF16 (round to nearest even) and stores with 8-byte
-// writes: the fused FP32 -> half epilogue.
+// Matrix cores: v_mfma_f32_16x16x32_{f16,bf16}.  Under the MI355X power limit
+// it sustains a higher clock than the 32x32x16 form on random data (it moves
+// half the accumulator bytes per FLOP), which is what the throughput of a
+// dense half-precision GEMM on this part is bound by.
 //
-// NN: B[K][N] arrives n-contiguous; each thread loads an 8 (k) x 8 (n) block
-// with eight 16-byte loads and transposes it in registers, so the LDS image of
-// the B tile is k-contiguous exactly as in TN and the inner loop is shared.
+// Global -> LDS: direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds), one
+// 1 KiB segment per wave instruction, no registers involved (the pages'
+// asynchronous gmem -> smem copies: cp.async in the HGEMM MMA note's main
+// loop section, TMA in the tcgen05 translation).  Rows past M/N and k past K
+// read as zero through the buffer range check.  The LDS holds a ring of three
+// A stages and two B stages (A and B of one K step of 64 are 32 KiB each for
+// a 256 x 256 tile, 160 KiB in all): the loads of A run two steps ahead and
+// the loads of B one step ahead -- the multi-stage pipeline of the HGEMM MMA
+// note and of the tcgen05 translation's pipelining section, sized to the
+// 160 KiB LDS of gfx950.  Each 128-byte row of a K step is stored with its
+// 16-byte chunks XOR-swizzled (chunk ^ ((row >> 1) & 7)), an LDS layout that
+// keeps both the 16-byte fragment reads and the direct-to-LDS writes free of
+// bank conflicts (the swizzle of the CuTe note's first step and the ablation
+// draft's section 3 bank analysis, redone for 64 banks).
 //
-// Workgroup order: an XCD-aware remap gives each of the 8 XCDs (which receive
-// workgroups round-robin) a contiguous range of tile ids, and the tile ids are
-// walked in groups of GROUP_M tile rows, so the tiles resident on one XCD at
-// the same time share A row panels and B column panels in its L2 (the block
-// swizzle of the HGEMM notes and the grouped order of the tcgen05
+// NN: B arrives k-major (n contiguous).  It is loaded into LDS as is and the
+// MFMA operand (8 consecutive k of one n per lane) is assembled with the
+// gfx950 transposing LDS read (ds_read_b64_tr_b16, two per fragment), so no
+// pass over the data transposes it.
+//
+// Schedule: one K step is 2 k-slices of 32, 2 * FM * FN MFMAs per wave.  The
+// instruction stream is ordered by hand (each MFMA followed by at most one
+// LDS read and/or one load, fenced with sched_barrier) so that every memory
+// instruction issues while the matrix core is busy.  The fragments of the
+// next slice are read during the current one (double buffer in registers);
+// the single workgroup barrier per step sits before the last half slice so
+// those MFMAs cover the first LDS reads of the next step.  The barrier is a
+// bare s_barrier with explicit waits: __syncthreads() would wait for every
+// load still in flight.
+//
+// Epilogue: FP32 -> FP16/BF16 (round to nearest even) into a wave-private,
+// padded LDS region, then 16-byte stores of whole 256-byte row segments (the
+// LDS-staged epilogue of the CuTe note and of the S4000 post).
+//
+// Workgroup order: XCD-aware remap plus grouping by group_m tile rows (see
+// tile_coords), so the tiles resident on one XCD share A and B panels in its
+// L2 (the block swizzle of the HGEMM notes, the grouped order of the tcgen05
 // translation's 2-SM section).
 #pragma once
 
-#include "device.hpp"
+#include <type_traits>
+
+#include "common.hpp"
 
 namespace hgemm {
 
-enum LdsLayout { kLdsXor = 0, kLdsPlain = 1, kLdsPad = 2 };
-enum Layout { kTN = 0, kNN = 1 };
-
-struct GemmArgs {
-  const uint16_t *A;
-  const uint16_t *B;
-  uint16_t *C;
-  int M, N, K;
-  int group_m;   // >= 1
-  int xcd_remap; // 0 or 1
-};
-
-template <int BM_, int BN_, int WM_, int WN_, int LDS_>
+template <int BM_, int BN_, int LDS_ = kLdsXor, int EPI_ = 1>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 64;
-  static constexpr int WM = WM_, WN = WN_;
-  static constexpr int NT = 64 * WM * WN;
-  static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
-  static constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 blocks per wave
+  static constexpr int NT = 256;                      // 4 waves, 2 x 2
+  static constexpr int WTM = BM / 2, WTN = BN / 2;    // wave block
+  static constexpr int FM = WTM / 16, FN = WTN / 16;  // 16x16 MFMA tiles per wave
+  static constexpr int NMF = FM * FN;                 // MFMAs per 32-k slice
   static constexpr int LDS = LDS_;
-  static constexpr int ROWB = (LDS == kLdsPad) ? 144 : 128;  // LDS bytes per tile row
-  static constexpr int STAGE = (BM + BN) * ROWB;
-  static constexpr int LDS_BYTES = 2 * STAGE;
-  static constexpr int ROWS_PER_PASS = NT / 8;           // rows covered by one load pass
-  static constexpr int LA = BM / ROWS_PER_PASS;           // A chunks per thread
-  static constexpr int LB = BN / ROWS_PER_PASS;           // Bt chunks per thread (TN)
-  static constexpr int NN_BLOCKS = BN;                    // 8x8 blocks in a 64 x BN tile (NN)
-  static_assert(WM * WN == 4, "four waves per workgroup");
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is made of 32x32 blocks");
-  static_assert(BM % ROWS_PER_PASS == 0 && BN % ROWS_PER_PASS == 0, "load passes");
-  static_assert(NN_BLOCKS <= NT, "one 8x8 block per thread at most");
+  static constexpr int EPI = EPI_;                    // 1: C through LDS, 0: direct stores
+  static constexpr int A_STAGE = BM * 128;            // BM rows x 64 k x 2 bytes
+  static constexpr int B_STAGE = BN * 128;            // TN: BN rows x 64 k; NN: 64 rows x BN
+  static constexpr int B_BASE = 3 * A_STAGE;          // three A stages, then two B stages
+  static constexpr int PIPE_BYTES = 3 * A_STAGE + 2 * B_STAGE;
+  static constexpr int CROW = WTN * 2 + 16;           // epilogue row pitch (bytes)
+  static constexpr int EPI_BYTES = EPI ? 4 * WTM * CROW : 0;
+  static constexpr int LDS_BYTES = PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES;
+  static constexpr int SEG_A = BM / 32;               // 1 KiB A segments per wave and step
+  static constexpr int SEG_B = BN / 32;               // 1 KiB B segments per wave and step
+  static constexpr int NN_ROWB = BN * 2;              // NN: bytes per k-row of B in LDS
+  static constexpr int NN_CPR = BN / 8;               // NN: 16-byte chunks per k-row
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && BM <= 256 && BN <= 256, "tile");
+  static_assert(FM % 2 == 0, "the slice is split in halves by A block");
+  static_assert(LDS_BYTES <= 163840, "160 KiB of LDS");
+  static_assert(LDS == kLdsXor || LDS == kLdsPlain, "layouts of this kernel");
 };
 
-// Physical 16-byte chunk position of logical chunk c in tile row r.
-template <int LDS>
-__device__ __forceinline__ int chunk_pos(int r, int c) {
-  if constexpr (LDS == kLdsXor) return c ^ (r & 7);
-  else return c;
-}
-
-// Map the dispatch index to (tile_m, tile_n).
-__host__ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n,
-                                                     int group_m, int xcd_remap, int &tm,
-                                                     int &tn) {
-  const int total = tiles_m * tiles_n;
-  if (xcd_remap) {
-    // workgroup i runs on XCD i % 8; give XCD x the ids [x*per, (x+1)*per)
-    const int per = total >> 3;
-    if (pid < (per << 3)) pid = (pid & 7) * per + (pid >> 3);
-  }
-  const int width = group_m * tiles_n;
-  const int g = pid / width;
-  const int first_m = g * group_m;
-  const int gsz = (tiles_m - first_m < group_m) ? tiles_m - first_m : group_m;
-  const int in = pid - g * width;
-  tm = first_m + in % gsz;
-  tn = in / gsz;
-}
-
 template <class T, int LAYOUT, int DT>
-__global__ __launch_bounds__(T::NT, 1) void gemm_kernel(GemmArgs args) {
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
-  constexpr int FM = T::FM, FN = T::FN, ROWB = T::ROWB;
-  constexpr int LA = T::LA, LB = T::LB;
-  __shared__ __attribute__((aligned(16))) char smem[T::LDS_BYTES];
+  constexpr int FM = T::FM, FN = T::FN, NMF = T::NMF;
+  constexpr int SEG_A = T::SEG_A, SEG_B = T::SEG_B;
+  constexpr bool NN = LAYOUT == kNN;
+  constexpr int NRB = NN ? 2 * FN : FN;               // LDS reads for the B fragments of a slice
+  constexpr int NR = NRB + FM;                        // LDS reads per slice
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
 
   const int M = args.M, N = args.N, K = args.K;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, args.group_m, args.xcd_remap, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / T::WN, wn = wave % T::WN;
-
-  // ---- global load addressing -------------------------------------------
-  // A panel: rows m0 .. m0+BM of A[M][K]; thread loads chunk kc = tid % 8 of
-  // rows tid/8 + i*ROWS_PER_PASS.
-  const int ld_row = tid >> 3, ld_kc = tid & 7;
-  const int rows_a = min(BM, M - m0);
+  // ---- direct-to-LDS loads ------------------------------------------------
+  // A (and TN B): segment s = 8 tile rows of 128 bytes; lane -> (row s*8 +
+  // lane/8, stored chunk lane%8), which holds logical k-chunk
+  // (lane%8) ^ swizzle(row).  Wave w loads segments w*SEG .. w*SEG+SEG-1.
+  const int seg_row = lane >> 3, pchunk = lane & 7;
+  uint32_t a_off[SEG_A];
+  int a_chunk[SEG_A];
+#pragma unroll
+  for (int i = 0; i < SEG_A; ++i) {
+    const int row = (wave * SEG_A + i) * 8 + seg_row;
+    a_chunk[i] = pchunk ^ (chunk_pos<T::LDS>(row, 0));
+    a_off[i] = (uint32_t)(row * K + a_chunk[i] * 8) * 2u;
+  }
+  uint32_t b_off[SEG_B];
+  int b_chunk[SEG_B];
+  // NN B: segment s = RPS k-rows of 2*BN bytes; lane -> (k-row s*RPS + lane/CPR,
+  // stored chunk lane%CPR) holding n-chunk (lane%CPR) ^ nn_chunk_xor(k).
+  constexpr int RPS = 1024 / T::NN_ROWB;
+#pragma unroll
+  for (int i = 0; i < SEG_B; ++i) {
+    if constexpr (!NN) {
+      const int row = (wave * SEG_B + i) * 8 + seg_row;
+      b_chunk[i] = pchunk ^ (chunk_pos<T::LDS>(row, 0));
+      b_off[i] = (uint32_t)(row * K + b_chunk[i] * 8) * 2u;
+    } else {
+      const int k = (wave * SEG_B + i) * RPS + lane / T::NN_CPR;
+      const int c = (lane % T::NN_CPR) ^ nn_chunk_xor<T::LDS>(k, T::NN_ROWB);
+      b_chunk[i] = c;
+      b_off[i] = (n0 + c * 8 < N) ? (uint32_t)(k * N + c * 8) * 2u : kOutOfRange;
+    }
+  }
   const uint16_t *a_panel = args.A + (size_t)m0 * K;
-  uint32_t a_off[LA];
-#pragma unroll
-  for (int i = 0; i < LA; ++i) a_off[i] = (uint32_t)((ld_row + i * T::ROWS_PER_PASS) * K + ld_kc * 8) * 2u;
+  const uint16_t *b_panel = NN ? args.B + n0 : args.B + (size_t)n0 * K;
 
-  // TN: Bt panel rows n0 .. n0+BN of Bt[N][K], same pattern as A.
-  // NN: thread owns the 8x8 block (k = nn_kg*8.., n = nn_nc*8..) of the 64 x BN tile.
-  const int rows_b = min(BN, N - n0);
-  uint32_t b_off[LAYOUT == kTN ? LB : 8];
-  const int nn_kg = tid & 7, nn_nc = tid >> 3;
-  const bool nn_active = (LAYOUT == kNN) && (tid < T::NN_BLOCKS);
-  if constexpr (LAYOUT == kTN) {
+  // A stage of step s at (s % 3) * A_STAGE, B stage at B_BASE + (s & 1) * B_STAGE
+  auto a_base = [&](int s) { return (uint32_t)((s % 3) * T::A_STAGE); };
+  auto b_base = [&](int s) { return (uint32_t)(T::B_BASE + (s & 1) * T::B_STAGE); };
+
+  __amdgpu_buffer_rsrc_t rs_a, rs_b;
+  int krem_a = 0, krem_b = 0;
+  auto prep_a = [&](int step) {
+    const int k0 = step * BK;
+    krem_a = K - k0;
+    rs_a = make_rsrc(a_panel + k0, krem_a > 0 ? (uint32_t)(rows_a * K - k0) * 2u : 0u);
+  };
+  auto prep_b = [&](int step) {
+    const int k0 = step * BK;
+    krem_b = K - k0;
+    if constexpr (!NN)
+      rs_b = make_rsrc(b_panel + k0, krem_b > 0 ? (uint32_t)(rows_b * K - k0) * 2u : 0u);
+    else  // k-rows k0 .. k0+63 of B[K][N]; rows past K fall outside
+      rs_b = make_rsrc(b_panel + (size_t)k0 * N, krem_b > 0 ? (uint32_t)(min(krem_b, BK) * N) * 2u : 0u);
+  };
+  auto load_a = [&](uint32_t stage, int i) {
+    // a chunk past K inside a valid row would read the next row: out of range
+    const uint32_t off = (a_chunk[i] * 8 < krem_a) ? a_off[i] : kOutOfRange;
+    load16_lds(rs_a, off, smem + stage + (wave * SEG_A + i) * 1024);
+  };
+  auto load_b = [&](uint32_t stage, int i) {
+    uint32_t off = b_off[i];
+    if constexpr (!NN) off = (b_chunk[i] * 8 < krem_b) ? off : kOutOfRange;
+    load16_lds(rs_b, off, smem + stage + (wave * SEG_B + i) * 1024);
+  };
+
+  // ---- fragment reads -------------------------------------------------------
+  // A / TN B: 16 rows x 32 k; lane reads row (lane & 15), logical k-chunk
+  // 4*slice + lane/16 of that row.
+  uint32_t rd_off[2];
 #pragma unroll
-    for (int i = 0; i < LB; ++i) b_off[i] = (uint32_t)((ld_row + i * T::ROWS_PER_PASS) * K + ld_kc * 8) * 2u;
-  } else {
-    const bool col_ok = nn_active && (n0 + nn_nc * 8 < N);
+  for (int sl = 0; sl < 2; ++sl)
+    rd_off[sl] = (lane & 15) * 128 + chunk_pos<T::LDS>(lane & 15, 4 * sl + (lane >> 4)) * 16;
+  const uint32_t rd_a = (wm * T::WTM) * 128;
+  const uint32_t rd_b = (wn * T::WTN) * 128;
+  // NN B: lane i of group g points at k-row 8g + i/4 (+4 for the second read)
+  // of slice sl, n = 16j + 4*(i%4) .. +3 of the wave's columns.
+  uint32_t tr_off[NN ? FN : 1];
+  if constexpr (NN) {
+    const int g = lane >> 4, i = lane & 15;
+    const int k = 8 * g + (i >> 2);
+    const int fx = nn_chunk_xor<T::LDS>(k, T::NN_ROWB);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      b_off[j] = col_ok ? (uint32_t)((nn_kg * 8 + j) * N + nn_nc * 8) * 2u : kOutOfRange;
+    for (int j = 0; j < FN; ++j) {
+      const int cbase = (wn * T::WTN + 16 * j) / 8;  // even chunk index
+      const int c = (cbase ^ fx) + ((i & 3) >> 1);
+      tr_off[j] = k * T::NN_ROWB + c * 16 + (i & 1) * 8;
+    }
   }
 
-  // ---- LDS addressing ----------------------------------------------------
-  // Stage s: A rows at s*STAGE, B rows at s*STAGE + BM*ROWB.
-  // Store position of this thread's chunk (A, and Bt for TN): row ld_row + i*RPP.
-  const uint32_t st_a = ld_row * ROWB + chunk_pos<T::LDS>(ld_row, ld_kc) * 16;
-  const uint32_t st_b = BM * ROWB + st_a;
-  // Fragment reads: lane reads row (sub-tile base + lane%32), logical chunk 2*ks + lane/32.
-  uint32_t rd_off[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    rd_off[ks] = (lane & 31) * ROWB + chunk_pos<T::LDS>(lane & 31, 2 * ks + (lane >> 5)) * 16;
-  const uint32_t rd_a = (wm * T::WTM) * ROWB;            // + i*32*ROWB
-  const uint32_t rd_b = BM * ROWB + (wn * T::WTN) * ROWB;  // + j*32*ROWB
-
-  u32x4 ra[LA];
-  u32x4 rb[LAYOUT == kTN ? LB : 8];
-
-  auto gload = [&](int k0, bool tail) {
-    const __amdgpu_buffer_rsrc_t rsa =
-        make_rsrc(a_panel + k0, (uint32_t)(rows_a * K - k0) * 2u);
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      uint32_t off = a_off[i];
-      if (tail && (k0 + ld_kc * 8 >= K)) off = kOutOfRange;
-      ra[i] = load16(rsa, off);
-    }
-    if constexpr (LAYOUT == kTN) {
-      const __amdgpu_buffer_rsrc_t rsb =
-          make_rsrc(args.B + (size_t)n0 * K + k0, (uint32_t)(rows_b * K - k0) * 2u);
-#pragma unroll
-      for (int i = 0; i < LB; ++i) {
-        uint32_t off = b_off[i];
-        if (tail && (k0 + ld_kc * 8 >= K)) off = kOutOfRange;
-        rb[i] = load16(rsb, off);
+  u32x4 f[2][FN + FM];  // [set][B fragments 0..FN-1, A fragments FN..FN+FM-1]
+  // read op q (0..NR-1) of slice sl into set S: B fragments first, then A
+  auto read_op = [&](auto S_, uint32_t ab, uint32_t bb, int sl, int q) {
+    constexpr int S = decltype(S_)::value;
+    if (q < NRB) {
+      if constexpr (!NN) {
+        f[S][q] = *(const u32x4 *)(smem + bb + rd_b + q * 16 * 128 + rd_off[sl]);
+      } else {
+        const int j = q >> 1, h = q & 1;
+        const u32x2 v = lds_read_tr16(smem + bb + tr_off[j] + (32 * sl + 4 * h) * T::NN_ROWB);
+        f[S][j][2 * h] = v[0];
+        f[S][j][2 * h + 1] = v[1];
       }
     } else {
-      // rows k0 .. min(K, k0+64) of B[K][N], columns from n0; rows past K
-      // fall outside the resource and read as zero.
-      const __amdgpu_buffer_rsrc_t rsb =
-          make_rsrc(args.B + (size_t)k0 * N + n0, (uint32_t)(min(K - k0, BK) * N) * 2u);
-      if (nn_active) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) rb[j] = load16(rsb, b_off[j]);
-      }
+      const int i = q - NRB;
+      f[S][FN + i] = *(const u32x4 *)(smem + ab + rd_a + i * 16 * 128 + rd_off[sl]);
     }
   };
 
-  auto swrite = [&](int stage) {
-    char *base = smem + stage * T::STAGE;
-#pragma unroll
-    for (int i = 0; i < LA; ++i)
-      *(u32x4 *)(base + st_a + i * T::ROWS_PER_PASS * ROWB) = ra[i];
-    if constexpr (LAYOUT == kTN) {
-#pragma unroll
-      for (int i = 0; i < LB; ++i)
-        *(u32x4 *)(base + st_b + i * T::ROWS_PER_PASS * ROWB) = rb[i];
-    } else {
-      if (nn_active) {
-        // transpose the 8x8 block: rb[j] holds n = nn_nc*8 + 0..7 at k = nn_kg*8 + j;
-        // tile row n gets the 8 k values as one 16-byte chunk (logical chunk nn_kg).
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int d = i >> 1;
-          u32x4 w;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const uint32_t lo = rb[2 * p][d], hi = rb[2 * p + 1][d];
-            w[p] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-          }
-          const int row = nn_nc * 8 + i;
-          *(u32x4 *)(base + BM * ROWB + row * ROWB + chunk_pos<T::LDS>(row, nn_kg) * 16) = w;
-        }
-      }
-    }
-  };
-
-  f32x16 acc[FM][FN];
+  f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{};
+  // MFMA t of a slice: A tile i = t / FN, B tile j = t % FN (operands swapped so
+  // each lane ends with 4 consecutive columns of one row of C)
+  auto mfma = [&](auto S_, int t) {
+    constexpr int S = decltype(S_)::value;
+    const int i = t / FN, j = t % FN;
+    acc[i][j] = mfma16x16x32<DT>(f[S][j], f[S][FN + i], acc[i][j]);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
   const int KT = (K + BK - 1) / BK;
-  const bool has_tail = (K % BK) != 0;
-  if (KT > 0) {
-    gload(0, has_tail && KT == 1);
-    swrite(0);
-  }
-  __syncthreads();
 
+  // ---- prologue: A of steps 0, 1 and B of step 0 in flight; slice 0 read ----
+  prep_a(0);
+#pragma unroll
+  for (int i = 0; i < SEG_A; ++i) load_a(a_base(0), i);
+  prep_b(0);
+#pragma unroll
+  for (int i = 0; i < SEG_B; ++i) load_b(b_base(0), i);
+  prep_a(1);
+#pragma unroll
+  for (int i = 0; i < SEG_A; ++i) load_a(a_base(1), i);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(SEG_A, 0));
+  wg_barrier();
+  prep_b(1);
+#pragma unroll
+  for (int q = 0; q < NR; ++q) {
+    read_op(I0{}, a_base(0), b_base(0), 0, q);
+    if (q * SEG_B / NR != (q + 1) * SEG_B / NR) load_b(b_base(1), q * SEG_B / NR);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- main loop -------------------------------------------------------------
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK, has_tail && (kt + 2 == KT));
-    const char *base = smem + cur * T::STAGE;
+    const uint32_t ca = a_base(kt), cb = b_base(kt);
+    const uint32_t na = a_base(kt + 1), nb = b_base(kt + 1);
+    // X: slice 0; read slice 1; A of step kt+2 into the stage step kt-1 used
+    prep_a(kt + 2);
+    const uint32_t la = a_base(kt + 2);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 fa[FM], fb[FN];
+    for (int t = 0; t < NMF; ++t) {
+      mfma(I0{}, t);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = *(const u32x4 *)(base + rd_a + i * 32 * ROWB + rd_off[ks]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = *(const u32x4 *)(base + rd_b + j * 32 * ROWB + rd_off[ks]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16<DT>(fb[j], fa[i], acc[i][j]);
+      for (int q = t * NR / NMF; q < (t + 1) * NR / NMF; ++q) read_op(I1{}, ca, cb, 1, q);
+      if constexpr (SEG_A > 0) {
+        constexpr int SP = NMF / SEG_A;  // one A load every SP MFMAs, after MFMA 2 mod SP
+        if (t % SP == (SP > 2 ? 2 : 0)) load_a(la, t / SP);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < KT) swrite(cur ^ 1);
-    __syncthreads();
+    // Y: first half of slice 1
+#pragma unroll
+    for (int t = 0; t < NMF / 2; ++t) {
+      mfma(I1{}, t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // step kt+1 complete in LDS (A of kt+2 may stay in flight), own reads done
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(SEG_A, 0));
+    wg_barrier();
+    // Z: second half of slice 1; read slice 0 of step kt+1; B of step kt+2
+    prep_b(kt + 2);
+    const uint32_t lb = b_base(kt + 2);
+#pragma unroll
+    for (int t = NMF / 2; t < NMF; ++t) {
+      mfma(I1{}, t);
+      constexpr int H = NMF / 2;
+      const int u = t - H;
+#pragma unroll
+      for (int q = u * NR / H; q < (u + 1) * NR / H; ++q) read_op(I0{}, na, nb, 0, q);
+      if constexpr (SEG_B > 0) {
+        constexpr int SP = H / SEG_B > 0 ? H / SEG_B : 1;
+        if (u % SP == (SP > 1 ? 1 : 0) && u / SP < SEG_B) load_b(lb, u / SP);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
-  // ---- epilogue: FP32 -> FP16/BF16, 8-byte stores -------------------------
-  // lane holds, for block (i, j) and group g, C[m][n .. n+3] with
-  // m = m0 + wm*WTM + i*32 + lane%32, n = n0 + wn*WTN + j*32 + 8g + 4*(lane/32).
+  // ---- epilogue --------------------------------------------------------------
+  // lane holds, for tile (i, j): C[m][n .. n+3], m = wave row + 16i + lane%16,
+  // n = wave column + 16j + 4*(lane/16)
+  const int wm0 = m0 + wm * T::WTM, wn0 = n0 + wn * T::WTN;
+  if constexpr (T::EPI) {
+    __builtin_amdgcn_s_waitcnt(0);  // no load still writing LDS, no read pending
+    wg_barrier();                   // every wave is done with the pipeline stages
+    char *cw = smem + wave * (T::WTM * T::CROW);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * T::WTM + i * 32 + (lane & 31);
-    if (m >= M) continue;
-    uint16_t *crow = args.C + (size_t)m * N;
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
+      for (int j = 0; j < FN; ++j) {
+        u32x2 v;
+        v[0] = pack2<DT>(acc[i][j][0], acc[i][j][1]);
+        v[1] = pack2<DT>(acc[i][j][2], acc[i][j][3]);
+        *(u32x2 *)(cw + (i * 16 + (lane & 15)) * T::CROW + (j * 16 + 4 * (lane >> 4)) * 2) = v;
+      }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    // each row of the wave block is WTN*2 bytes = WTN/8 lanes of 16 bytes
+    constexpr int LPR = T::WTN / 8, RPI = 64 / LPR;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * T::WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+    for (int r = 0; r < T::WTM / RPI; ++r) {
+      const int row = r * RPI + lane / LPR, col = 8 * (lane % LPR);
+      const u32x4 v = *(const u32x4 *)(cw + row * T::CROW + col * 2);
+      const int m = wm0 + row, n = wn0 + col;
+      if (m < M && n < N) *(u32x4 *)(args.C + (size_t)m * N + n) = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = wm0 + i * 16 + (lane & 15);
+      if (m >= M) continue;
+      uint16_t *crow = args.C + (size_t)m * N;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = wn0 + j * 16 + 4 * (lane >> 4);
         if (n < N) {
           u32x2 v;
-          v[0] = pack2<DT>(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-          v[1] = pack2<DT>(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          v[0] = pack2<DT>(acc[i][j][0], acc[i][j][1]);
+          v[1] = pack2<DT>(acc[i][j][2], acc[i][j][3]);
           *(u32x2 *)(crow + n) = v;
         }
       }

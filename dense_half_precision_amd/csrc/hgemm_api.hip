@@ -8,6 +8,7 @@
 
 #include "hgemm.h"
 #include "gemm_kernel.hpp"
+#include "gemm_regstage.hpp"
 
 namespace {
 
@@ -28,32 +29,47 @@ constexpr KernelEntry entry(const char *name, int group_m) {
   return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m,
                      &gemm_kernel<T, LAYOUT, DT>};
 }
+template <class T, int LAYOUT, int DT>
+constexpr KernelEntry rs_entry(const char *name, int group_m) {
+  return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m,
+                     &regstage_kernel<T, LAYOUT, DT>};
+}
 
-using T256 = TileCfg<256, 256, 2, 2, kLdsXor>;
-using T256Plain = TileCfg<256, 256, 2, 2, kLdsPlain>;
-using T256Pad = TileCfg<256, 256, 2, 2, kLdsPad>;
-using T128 = TileCfg<128, 128, 2, 2, kLdsXor>;
-using T64 = TileCfg<64, 64, 2, 2, kLdsXor>;
+using T256 = TileCfg<256, 256>;
+using T128 = TileCfg<128, 128>;
+using T64 = TileCfg<64, 64>;
+using T256Plain = TileCfg<256, 256, kLdsPlain>;
+using T256Direct = TileCfg<256, 256, kLdsXor, 0>;
+using R256 = RsCfg<256, 256, 2, 2, kLdsXor>;
+using R256Plain = RsCfg<256, 256, 2, 2, kLdsPlain>;
+using R256Pad = RsCfg<256, 256, 2, 2, kLdsPad>;
+using R256XorRow = RsCfg<256, 256, 2, 2, kLdsXorRow>;
 
 // Index order is part of the ablation interface (hgemm_kernel_info lists it).
+// Entries 0..11 are the production kernels the automatic choice picks from.
 const KernelEntry kTable[] = {
-    entry<T256, kTN, kF16>("tn_f16_256x256x64_xor", 8),
-    entry<T256, kTN, kBF16>("tn_bf16_256x256x64_xor", 8),
-    entry<T256, kNN, kF16>("nn_f16_256x256x64_xor", 8),
-    entry<T256, kNN, kBF16>("nn_bf16_256x256x64_xor", 8),
-    entry<T128, kTN, kF16>("tn_f16_128x128x64_xor", 8),
-    entry<T128, kTN, kBF16>("tn_bf16_128x128x64_xor", 8),
-    entry<T128, kNN, kF16>("nn_f16_128x128x64_xor", 8),
-    entry<T128, kNN, kBF16>("nn_bf16_128x128x64_xor", 8),
-    entry<T64, kTN, kF16>("tn_f16_64x64x64_xor", 8),
-    entry<T64, kTN, kBF16>("tn_bf16_64x64x64_xor", 8),
-    entry<T64, kNN, kF16>("nn_f16_64x64x64_xor", 8),
-    entry<T64, kNN, kBF16>("nn_bf16_64x64x64_xor", 8),
-    // LDS-layout ablations of the main tile (unswizzled rows, padded rows)
-    entry<T256Plain, kTN, kF16>("tn_f16_256x256x64_plain", 8),
-    entry<T256Pad, kTN, kF16>("tn_f16_256x256x64_pad", 8),
-    entry<T256Plain, kNN, kBF16>("nn_bf16_256x256x64_plain", 8),
-    entry<T256Pad, kNN, kBF16>("nn_bf16_256x256x64_pad", 8),
+    entry<T256, kTN, kF16>("tn_f16_256x256x64", 4),
+    entry<T256, kTN, kBF16>("tn_bf16_256x256x64", 4),
+    entry<T256, kNN, kF16>("nn_f16_256x256x64", 4),
+    entry<T256, kNN, kBF16>("nn_bf16_256x256x64", 4),
+    entry<T128, kTN, kF16>("tn_f16_128x128x64", 4),
+    entry<T128, kTN, kBF16>("tn_bf16_128x128x64", 4),
+    entry<T128, kNN, kF16>("nn_f16_128x128x64", 4),
+    entry<T128, kNN, kBF16>("nn_bf16_128x128x64", 4),
+    entry<T64, kTN, kF16>("tn_f16_64x64x64", 4),
+    entry<T64, kTN, kBF16>("tn_bf16_64x64x64", 4),
+    entry<T64, kNN, kF16>("nn_f16_64x64x64", 4),
+    entry<T64, kNN, kBF16>("nn_bf16_64x64x64", 4),
+    // ablations of the production kernel: unswizzled LDS, direct epilogue stores
+    entry<T256Plain, kTN, kF16>("tn_f16_256x256x64_plainlds", 4),
+    entry<T256Plain, kNN, kBF16>("nn_bf16_256x256x64_plainlds", 4),
+    entry<T256Direct, kTN, kF16>("tn_f16_256x256x64_directepi", 4),
+    // baseline design: register-staged loads, 32x32x16 MFMA, LDS layout variants
+    rs_entry<R256, kTN, kF16>("rs_tn_f16_256x256x64_xor", 8),
+    rs_entry<R256Plain, kTN, kF16>("rs_tn_f16_256x256x64_plain", 8),
+    rs_entry<R256Pad, kTN, kF16>("rs_tn_f16_256x256x64_pad", 8),
+    rs_entry<R256XorRow, kTN, kF16>("rs_tn_f16_256x256x64_xorrow", 8),
+    rs_entry<R256, kNN, kBF16>("rs_nn_bf16_256x256x64_xor", 8),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -61,11 +77,11 @@ constexpr int64_t kMaxM = int64_t(1) << 30;
 constexpr int64_t kMaxN = int64_t(1) << 23;
 constexpr int64_t kMaxK = int64_t(1) << 21;
 
-int find_kernel(int layout, int dtype, int bm, int lds) {
-  for (int i = 0; i < kTableSize; ++i)
-    if (kTable[i].layout == layout && kTable[i].dtype == dtype && kTable[i].bm == bm &&
-        kTable[i].lds == lds)
-      return i;
+constexpr int kProductionKernels = 12;
+
+int find_kernel(int layout, int dtype, int bm) {
+  for (int i = 0; i < kProductionKernels; ++i)
+    if (kTable[i].layout == layout && kTable[i].dtype == dtype && kTable[i].bm == bm) return i;
   return -1;
 }
 
@@ -78,7 +94,7 @@ int auto_kernel(int layout, int dtype, int64_t M, int64_t N) {
   if (t256 >= 256) bm = 256;
   else if (t128 >= 128) bm = 128;
   else bm = 64;
-  return find_kernel(layout, dtype, bm, kLdsXor);
+  return find_kernel(layout, dtype, bm);
 }
 
 hgemm_status_t validate(int64_t M, int64_t N, int64_t K, int dtype, const void *A,

@@ -5,7 +5,7 @@
 #include <stdint.h>
 
 #include "hgemm_probe.h"
-#include "gemm_kernel.hpp"
+#include "gemm_regstage.hpp"
 
 namespace {
 
@@ -23,7 +23,7 @@ __global__ __launch_bounds__(64) void probe_mfma_kernel(const u32x4 *x, const u3
 // Same store/read pattern as gemm_kernel's A region with BM = 256, 256 threads.
 template <int LDS>
 __global__ __launch_bounds__(256) void probe_lds_kernel(const u32x4 *src, u32x4 *dst) {
-  using T = TileCfg<256, 256, 2, 2, LDS>;
+  using T = RsCfg<256, 256, 2, 2, LDS>;
   constexpr int ROWB = T::ROWB;
   __shared__ __attribute__((aligned(16))) char smem[256 * ROWB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -45,6 +45,108 @@ __global__ __launch_bounds__(256) void probe_lds_kernel(const u32x4 *src, u32x4 
       dst[(row0 + (lane & 31)) * 8 + 2 * ks + (lane >> 5)] = v;
     }
   }
+}
+
+__global__ __launch_bounds__(256) void probe_mfma_peak_kernel(int iters, float *out,
+                                                              uint64_t *clocks) {
+  const int t = threadIdx.x;
+  const uint64_t c0 = clock64(), r0 = wall_clock64();
+  u32x4 a = {0x3c003c00u ^ (uint32_t)t, 0x3c00u, 0x3c003c00u, 0x0u};
+  u32x4 b = {0x3c00u, 0x3c003c00u ^ (uint32_t)t, 0x0u, 0x3c003c00u};
+  f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j & 3] = mfma32x32x16<kF16>(a, b, acc[j & 3]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  out[blockIdx.x * 256 + t] = s;
+  const uint64_t c1 = clock64(), r1 = wall_clock64();
+  if (clocks != nullptr && (t & 63) == 0) {
+    const int w = blockIdx.x * 4 + (t >> 6);
+    clocks[2 * w] = c1 - c0;      // shader clock cycles
+    clocks[2 * w + 1] = r1 - r0;  // constant-rate real-time ticks
+  }
+}
+
+template <int PATTERN>
+__global__ __launch_bounds__(256) void probe_lds_read_kernel(int iters, float *out) {
+  __shared__ __attribute__((aligned(16))) char smem[65536];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int i = t; i < 65536 / 16; i += 256) ((u32x4 *)smem)[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  uint32_t off[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if constexpr (PATTERN == 0)
+      off[ks] = wave * 16384 + ks * 4096 + lane * 16;
+    else
+      off[ks] = wave * 16384 + (lane & 31) * 128 +
+                chunk_pos<PATTERN == 1 ? kLdsXor : (PATTERN == 2 ? kLdsPlain : kLdsXorRow)>(
+                    lane & 31, 2 * ks + (lane >> 5)) * 16;
+  }
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      // each wave stays inside its own 16 KiB quarter: pattern 0 spans
+      // 4 x 4096 + 3 x 1024 + 1024 bytes, patterns 1/2 span 4 x 4096 (32 rows each)
+      constexpr int kStep = (PATTERN == 0) ? 1024 : 4096;
+      const u32x4 v = *(const u32x4 *)(smem + off[j & 3] + (j >> 2) * kStep);
+      acc ^= v;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): keep reads of one iteration together
+  }
+  out[blockIdx.x * 256 + t] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+}
+
+// Streams 64 KiB per workgroup per iteration out of an L2-resident window:
+// MODE 0 into registers, MODE 1 straight into LDS; NF loads per lane in flight.
+template <int MODE, int NF>
+__global__ __launch_bounds__(256) void probe_l2_kernel(const uint16_t *buf, uint32_t window,
+                                                       uint32_t row_stride, int iters, float *out) {
+  __shared__ __attribute__((aligned(1024))) char smem[65536];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(buf, window);
+  const uint32_t mask = window - 1;  // window is a power of two
+  uint32_t base = (blockIdx.x * 65536u) & mask;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 16; j += NF) {
+      u32x4 v[NF];
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        // 1 KiB per wave and load: 8 rows of 128 bytes, rows row_stride bytes apart
+        const uint32_t off = (base + (uint32_t)(wave * 16 + j + i) * 8u * row_stride +
+                              (uint32_t)(lane >> 3) * row_stride + (uint32_t)(lane & 7) * 16u) & mask;
+        if constexpr (MODE == 0) v[i] = load16(r, off);
+        else load16_lds(r, off, smem + (wave * 16 + j + i) * 1024);
+      }
+      if constexpr (MODE == 0) {
+#pragma unroll
+        for (int i = 0; i < NF; ++i) acc ^= v[i];
+      }
+    }
+    if constexpr (MODE == 1) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    base = (base + 128u * 8u) & mask;  // next 128-byte column of the same rows
+  }
+  if constexpr (MODE == 1) {
+    __syncthreads();
+    acc = *(const u32x4 *)(smem + t * 16);
+  }
+  out[blockIdx.x * 256 + t] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+}
+
+template <int LDS>
+void lds_offsets(int rows, int *offsets) {
+  using T = RsCfg<256, 256, 2, 2, LDS>;
+  for (int r = 0; r < rows; ++r)
+    for (int c = 0; c < 8; ++c) offsets[r * 8 + c] = r * T::ROWB + chunk_pos<LDS>(r, c) * 16;
 }
 
 hgemm_status_t launched() {
@@ -86,10 +188,68 @@ hgemm_status_t hgemm_probe_lds_roundtrip(int lds_layout, const void *src, void *
       hipLaunchKernelGGL(probe_lds_kernel<kLdsPad>, dim3(1), dim3(256), 0, s, (const u32x4 *)src,
                          (u32x4 *)dst);
       break;
+    case kLdsXorRow:
+      hipLaunchKernelGGL(probe_lds_kernel<kLdsXorRow>, dim3(1), dim3(256), 0, s,
+                         (const u32x4 *)src, (u32x4 *)dst);
+      break;
     default:
       return HGEMM_ERR_INVALID_ARG;
   }
   return launched();
+}
+
+hgemm_status_t hgemm_probe_mfma_peak(int waves, int iters, float *out, uint64_t *clocks,
+                                     void *stream) {
+  if (waves <= 0 || waves % 4 != 0 || iters <= 0 || !out) return HGEMM_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(probe_mfma_peak_kernel, dim3(waves / 4), dim3(256), 0, (hipStream_t)stream,
+                     iters, out, clocks);
+  return launched();
+}
+
+hgemm_status_t hgemm_probe_lds_read(int workgroups, int iters, int pattern, float *out,
+                                    void *stream) {
+  if (workgroups <= 0 || iters <= 0 || !out) return HGEMM_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  switch (pattern) {
+    case 0: hipLaunchKernelGGL(probe_lds_read_kernel<0>, dim3(workgroups), dim3(256), 0, s, iters, out); break;
+    case 1: hipLaunchKernelGGL(probe_lds_read_kernel<1>, dim3(workgroups), dim3(256), 0, s, iters, out); break;
+    case 2: hipLaunchKernelGGL(probe_lds_read_kernel<2>, dim3(workgroups), dim3(256), 0, s, iters, out); break;
+    case 3: hipLaunchKernelGGL(probe_lds_read_kernel<3>, dim3(workgroups), dim3(256), 0, s, iters, out); break;
+    default: return HGEMM_ERR_INVALID_ARG;
+  }
+  return launched();
+}
+
+hgemm_status_t hgemm_probe_l2_read(int workgroups, int iters, int mode, const void *buf,
+                                   uint32_t window_bytes, uint32_t row_stride, float *out,
+                                   void *stream) {
+  if (workgroups <= 0 || iters <= 0 || !buf || !out) return HGEMM_ERR_INVALID_ARG;
+  if (row_stride < 128u || (row_stride & 15u)) return HGEMM_ERR_INVALID_ARG;
+  if (window_bytes < 65536u || window_bytes > (1u << 30) || (window_bytes & (window_bytes - 1)))
+    return HGEMM_ERR_INVALID_ARG;
+  if (((uintptr_t)buf) & 15) return HGEMM_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  const uint16_t *b = (const uint16_t *)buf;
+  switch (mode) {
+    case 0: hipLaunchKernelGGL((probe_l2_kernel<0, 16>), dim3(workgroups), dim3(256), 0, s, b, window_bytes, row_stride, iters, out); break;
+    case 1: hipLaunchKernelGGL((probe_l2_kernel<1, 16>), dim3(workgroups), dim3(256), 0, s, b, window_bytes, row_stride, iters, out); break;
+    case 2: hipLaunchKernelGGL((probe_l2_kernel<0, 8>), dim3(workgroups), dim3(256), 0, s, b, window_bytes, row_stride, iters, out); break;
+    case 3: hipLaunchKernelGGL((probe_l2_kernel<1, 8>), dim3(workgroups), dim3(256), 0, s, b, window_bytes, row_stride, iters, out); break;
+    default: return HGEMM_ERR_INVALID_ARG;
+  }
+  return launched();
+}
+
+hgemm_status_t hgemm_probe_lds_offsets(int lds_layout, int rows, int *offsets) {
+  if (rows <= 0 || !offsets) return HGEMM_ERR_INVALID_ARG;
+  switch (lds_layout) {
+    case kLdsXor: lds_offsets<kLdsXor>(rows, offsets); break;
+    case kLdsPlain: lds_offsets<kLdsPlain>(rows, offsets); break;
+    case kLdsPad: lds_offsets<kLdsPad>(rows, offsets); break;
+    case kLdsXorRow: lds_offsets<kLdsXorRow>(rows, offsets); break;
+    default: return HGEMM_ERR_INVALID_ARG;
+  }
+  return HGEMM_OK;
 }
 
 hgemm_status_t hgemm_probe_tile_order(int tiles_m, int tiles_n, int group_m, int xcd_remap,

@@ -19,7 +19,7 @@ F16, BF16 = 0, 1
 TN, NN = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 DTYPE_CODES = {"f16": F16, "fp16": F16, "float16": F16, "bf16": BF16, "bfloat16": BF16}
-LDS_XOR, LDS_PLAIN, LDS_PAD = 0, 1, 2
+LDS_XOR, LDS_PLAIN, LDS_PAD, LDS_XOR_ROW = 0, 1, 2, 3
 
 
 class HgemmError(RuntimeError):
@@ -68,6 +68,14 @@ def _lib() -> ctypes.CDLL:
     lib.hgemm_probe_mfma.restype = i32
     lib.hgemm_probe_lds_roundtrip.argtypes = [i32, vp, vp, vp]
     lib.hgemm_probe_lds_roundtrip.restype = i32
+    lib.hgemm_probe_mfma_peak.argtypes = [i32, i32, vp, vp, vp]
+    lib.hgemm_probe_mfma_peak.restype = i32
+    lib.hgemm_probe_lds_read.argtypes = [i32, i32, i32, vp, vp]
+    lib.hgemm_probe_lds_read.restype = i32
+    lib.hgemm_probe_l2_read.argtypes = [i32, i32, i32, vp, ctypes.c_uint32, ctypes.c_uint32, vp, vp]
+    lib.hgemm_probe_l2_read.restype = i32
+    lib.hgemm_probe_lds_offsets.argtypes = [i32, i32, ip]
+    lib.hgemm_probe_lds_offsets.restype = i32
     lib.hgemm_probe_tile_order.argtypes = [i32, i32, i32, i32, ip, ip]
     lib.hgemm_probe_tile_order.restype = i32
     _LIB = lib
@@ -220,3 +228,10 @@ def tile_order(tiles_m, tiles_n, group_m, xcd_remap):
     _check(_lib().hgemm_probe_tile_order(tiles_m, tiles_n, group_m, xcd_remap, tm, tn),
            "hgemm_probe_tile_order")
     return list(tm), list(tn)
+
+
+def lds_offsets(lds_layout, rows=256):
+    """offsets[r][c]: byte offset of chunk c of tile row r in an LDS stage."""
+    buf = (ctypes.c_int * (rows * 8))()
+    _check(_lib().hgemm_probe_lds_offsets(lds_layout, rows, buf), "hgemm_probe_lds_offsets")
+    return [list(buf[r * 8:(r + 1) * 8]) for r in range(rows)]

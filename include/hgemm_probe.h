@@ -33,7 +33,8 @@ hgemm_status_t hgemm_probe_mfma(int dtype, const void *x, const void *y, float *
 /*
  * LDS layout round trip for a 256-row x 64-column tile of 16-bit values:
  * the tile is written to LDS with the kernels' store pattern and LDS layout
- * `lds_layout` (0 = XOR swizzle, 1 = plain rows, 2 = padded rows), read back
+ * `lds_layout` (0 = XOR swizzle on row/2, 1 = plain rows, 2 = padded rows,
+ * 3 = XOR swizzle on the row), read back
  * with the kernels' operand-fragment pattern, and each fragment is stored
  * to `dst` at the logical position it is meant to hold.  dst must equal src
  * (the round-trip check of the tcgen05 translation's swizzle section).
@@ -41,6 +42,55 @@ hgemm_status_t hgemm_probe_mfma(int dtype, const void *x, const void *y, float *
  */
 hgemm_status_t hgemm_probe_lds_roundtrip(int lds_layout, const void *src, void *dst,
                                          void *stream);
+
+/*
+ * Matrix-core throughput ceiling: `waves` 64-lane waves (in workgroups of 4)
+ * each issue `iters` x 16 independent 32x32x16 FP16 MFMAs with no memory
+ * traffic in the loop.  FLOPs = waves * iters * 16 * 32768.  out receives
+ * one float per lane (a sum that keeps the work alive), waves*64 floats.
+ * clocks (may be NULL): per wave, the shader-clock cycles and the ticks of
+ * the constant-rate real-time counter its loop took (2*waves uint64), from
+ * which the sustained engine clock follows.
+ */
+hgemm_status_t hgemm_probe_mfma_peak(int waves, int iters, float *out, uint64_t *clocks,
+                                     void *stream);
+
+/*
+ * LDS read throughput of one 16-byte-per-lane access pattern, over a
+ * 64 KiB buffer per workgroup of 256 threads, `iters` x 16 reads per lane:
+ *   pattern 0: lane-contiguous (lane l reads bytes 16*l .. of a 1 KiB row),
+ *   pattern 1: the GEMM operand-fragment read with the XOR swizzle,
+ *   pattern 2: the same read on plain (unswizzled) 128-byte rows,
+ *   pattern 3: the same read with the chunk ^ (row & 7) swizzle.
+ * Bytes read = workgroups * 256 * iters * 16 * 16.  out: workgroups*256
+ * floats.
+ */
+hgemm_status_t hgemm_probe_lds_read(int workgroups, int iters, int pattern, float *out,
+                                    void *stream);
+
+/*
+ * Global-to-CU streaming throughput: every workgroup of 256 threads moves
+ * 64 KiB per iteration (16 x 16 bytes per lane) out of the window
+ * [buf, buf + window_bytes) (a power of two between 64 KiB and 1 GiB; small
+ * windows stay resident in L2), for `iters` iterations.  Each wave-wide load
+ * reads 8 rows of 128 bytes whose starts are row_stride bytes apart (a
+ * multiple of 16, >= 128; 128 = contiguous, 2*K = one K-step of a GEMM
+ * operand); successive iterations move to the next 128-byte column.
+ *   mode 0: into registers, 16 loads per lane in flight,
+ *   mode 1: straight into LDS (direct-to-LDS loads), 16 in flight,
+ *   mode 2: into registers, 8 in flight,  mode 3: into LDS, 8 in flight.
+ * Bytes moved = workgroups * iters * 65536.  out: workgroups*256 floats.
+ */
+hgemm_status_t hgemm_probe_l2_read(int workgroups, int iters, int mode, const void *buf,
+                                   uint32_t window_bytes, uint32_t row_stride, float *out,
+                                   void *stream);
+
+/*
+ * Host-only: byte offset, inside one LDS stage, of 16-byte chunk c of tile
+ * row r under LDS layout `lds_layout` (as in hgemm_probe_lds_roundtrip), for
+ * r < rows and c < 8: offsets[r * 8 + c].  No GPU work.
+ */
+hgemm_status_t hgemm_probe_lds_offsets(int lds_layout, int rows, int *offsets);
 
 /*
  * Host-only: the workgroup -> output-tile order the GEMM kernels use for a

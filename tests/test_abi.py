@@ -76,7 +76,8 @@ def test_kernel_table_and_auto_choice():
     for k in tab:
         assert k["layout"] in (0, 1) and k["dtype"] in (0, 1) and k["bk"] == 64
         lay = "tn" if k["layout"] == 0 else "nn"
-        assert k["name"].startswith(f"{lay}_{'f16' if k['dtype'] == 0 else 'bf16'}_")
+        stem = k["name"][3:] if k["name"].startswith("rs_") else k["name"]
+        assert stem.startswith(f"{lay}_{'f16' if k['dtype'] == 0 else 'bf16'}_")
     # every layout/dtype has an automatic choice, matching layout and dtype
     for lay in (0, 1):
         for dt in (0, 1):

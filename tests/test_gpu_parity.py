@@ -57,7 +57,7 @@ def test_edge_shapes_auto(layout, dtype):
         helpers.parity(C, oracle.hgemm(layout, dtype, A, B), dtype, f"{layout} {dtype} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("kernel", range(16))
+@pytest.mark.parametrize("kernel", range(24))
 def test_every_kernel_ragged(kernel):
     tab = hgemm.kernel_table()
     if kernel >= len(tab):

@@ -60,7 +60,7 @@ def test_mfma_k_order_is_shared():
         assert np.all(dd.cpu().numpy() == 2.0), f"k={k}"
 
 
-@pytest.mark.parametrize("layout", [hgemm.LDS_XOR, hgemm.LDS_PLAIN, hgemm.LDS_PAD])
+@pytest.mark.parametrize("layout", [hgemm.LDS_XOR, hgemm.LDS_PLAIN, hgemm.LDS_PAD, hgemm.LDS_XOR_ROW])
 def test_lds_roundtrip(layout):
     import torch
     src = np.random.Generator(np.random.PCG64(4)).integers(0, 65536, size=(256, 64)).astype(np.uint16)
