@@ -40,7 +40,7 @@ def build(verbose: bool = False) -> str:
 
 def asm(source: str = "hgemm_api.hip", out: str | None = None) -> str:
     """Device assembly of one source (for reading our own ISA)."""
-    out = out or os.path.join(ROOT, "_work", source.replace(".hip", ".s"))
+    out = out or os.path.join(PKG, "_build", source.replace(".hip", ".s"))
     os.makedirs(os.path.dirname(out), exist_ok=True)
     cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "-S", "--cuda-device-only",
            os.path.join(CSRC, source), "-o", out]

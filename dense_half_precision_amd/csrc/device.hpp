@@ -51,14 +51,31 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 x, u32x4 y, f32x4 c) {
   }
 }
 
-// Transposing LDS read of 16-bit data (ds_read_b64_tr_b16).  Within each group
-// of 16 lanes, lane i points at 4 consecutive elements; lane l receives element
-// (l % 4) of the row that lane 4*j + l/4 points at, for j = 0..3.  Addresses
-// are byte offsets into the workgroup's LDS, 8-byte aligned.
-__device__ __forceinline__ u32x2 lds_read_tr16(const void *lds_ptr) {
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4 *)(lds_ptr));
-  return __builtin_bit_cast(u32x2, v);
+// Byte address of a location in the workgroup's LDS (the 32-bit address that
+// ds_* instructions take).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)(p);
+}
+
+// Transposing LDS read of 16-bit data (ds_read_b64_tr_b16) at LDS byte address
+// addr + off (off a constant below 65536 after inlining; the build fails
+// otherwise).  Within each group of 16 lanes, lane i points at 4 consecutive
+// elements; lane l receives element (l % 4) of the row that lane 4*j + l/4
+// points at, for j = 0..3.  Addresses are 8-byte aligned.
+//
+// Issued as inline assembly: the compiler's wait-count pass cannot tell this
+// instruction's builtin form apart from a read of memory that a pending
+// direct-to-LDS load may still be writing, and drains every load in flight
+// (vmcnt(0)) before it, which serialises the load pipeline.  The pass does not
+// see the assembly either, so it inserts no wait for the destination: the
+// caller must issue a compiler-visible LDS read after this one and consume the
+// destination only in instructions that also need that later read.  LDS reads
+// complete in order, so the wait the compiler places for the later read also
+// covers this one.  The memory clobber keeps the two in program order.
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr, int off) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(off) : "memory");
+  return v;
 }
 
 // Two FP32 values -> packed pair of 16-bit values, round to nearest even

@@ -201,7 +201,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
         f[S][q] = *(const u32x4 *)(smem + bb + rd_b + q * 16 * 128 + rd_off[sl]);
       } else {
         const int j = q >> 1, h = q & 1;
-        const u32x2 v = lds_read_tr16(smem + bb + tr_off[j] + (32 * sl + 4 * h) * T::NN_ROWB);
+        // every MFMA that takes this B fragment also takes an A fragment of the
+        // same slice, read below (q >= NRB): its wait covers this read
+        const u32x2 v = lds_read_tr16(lds_addr(smem + bb + tr_off[j]), (32 * sl + 4 * h) * T::NN_ROWB);
         f[S][j][2 * h] = v[0];
         f[S][j][2 * h + 1] = v[1];
       }
@@ -291,6 +293,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+
+  // The last step (or, for K = 0, the prologue) read fragments for a step that
+  // does not exist; the compiler sees those values dead and may hand their
+  // registers to the epilogue while the transposing reads, which it does not
+  // track, still write them.  Wait for them here, and keep the B fragment
+  // registers alive up to the wait.
+  if constexpr (NN) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0][0]));
+#pragma unroll
+    for (int j = 1; j < FN; ++j) asm volatile("" : "+v"(f[0][j]));
   }
 
   // ---- epilogue --------------------------------------------------------------
