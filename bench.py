@@ -70,6 +70,48 @@ def cpu_baseline(w, A, B, budget_s: float):
                       f"elements, FP64 accumulation) in {dt:.1f} s"}
 
 
+def oracle_table(only: int = 0) -> int:
+    """CPU oracle timings per workload on this host (no GPU involved): full
+    output for the three smaller workloads (and the smallest on one thread, in
+    a child process), the 4096-element sample check and one band of M/64 full
+    rows, extrapolated x64, for the two largest.  One JSON line each."""
+    import subprocess
+    import numpy as np
+    import oracle
+    from dense_half_precision_amd import inputs
+    oracle.build(0, force=False)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    for w in inputs.WORKLOADS:
+        if only and w.index != only:
+            continue
+        A, B = inputs.operands(w)
+        rec = {"oracle_table": w.name, "threads": threads, "cpu_count": os.cpu_count()}
+        if w.M * w.N * w.K <= 4096 ** 3:
+            t0 = time.perf_counter()
+            oracle.hgemm(w.layout, w.dtype, A, B)
+            dt = time.perf_counter() - t0
+            rec.update(full_s=round(dt, 4), gflops=round(w.flops / dt / 1e9, 2))
+        else:
+            rows, cols = inputs.stratified_samples(w.M, w.N, inputs.SAMPLE_SEED_BASE + w.index)
+            t0 = time.perf_counter()
+            oracle.hgemm_sampled(w.layout, w.dtype, A, B, rows, cols)
+            rec["sample4096_s"] = round(time.perf_counter() - t0, 4)
+            band = w.M // 64
+            t0 = time.perf_counter()
+            oracle.hgemm(w.layout, w.dtype, A, B, rows=(0, band))
+            dt = time.perf_counter() - t0
+            rec.update(band_rows=band, band_s=round(dt, 4), full_s_extrapolated=round(64 * dt, 2),
+                       gflops=round(w.flops / (64 * dt) / 1e9, 2))
+        print(json.dumps(rec), flush=True)
+        if w.index == 1 and threads > 1 and not only:
+            env = dict(os.environ, OMP_NUM_THREADS="1")
+            r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-table",
+                                "--workload", "1"], env=env)
+            if r.returncode != 0:
+                return r.returncode
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,7 +126,11 @@ def main() -> int:
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the GEMM, run a plain device copy of this many MiB "
                          "(reference point for scaling FETCH_SIZE/WRITE_SIZE counters)")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="time the CPU oracle on every workload (host only) and exit")
     args = ap.parse_args()
+    if args.oracle_table:
+        return oracle_table(args.workload if "--workload" in sys.argv else 0)
 
     if args.gpus != 1:
         print(f"bench.py: this HGEMM runs on one GPU; --gpus {args.gpus} is not supported "
