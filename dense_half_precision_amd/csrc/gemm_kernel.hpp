@@ -158,14 +158,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
       rs_b = make_rsrc(b_panel + (size_t)k0 * N, krem_b > 0 ? (uint32_t)(min(krem_b, BK) * N) * 2u : 0u);
   };
   auto load_a = [&](uint32_t stage, int i) {
-    // a chunk past K inside a valid row would read the next row: out of range
-    const uint32_t off = (a_chunk[i] * 8 < krem_a) ? a_off[i] : kOutOfRange;
-    load16_lds(rs_a, off, smem + stage + (wave * SEG_A + i) * 1024);
+    load16_lds(rs_a, a_off[i], smem + stage + (wave * SEG_A + i) * 1024);
   };
   auto load_b = [&](uint32_t stage, int i) {
-    uint32_t off = b_off[i];
-    if constexpr (!NN) off = (b_chunk[i] * 8 < krem_b) ? off : kOutOfRange;
-    load16_lds(rs_b, off, smem + stage + (wave * SEG_B + i) * 1024);
+    load16_lds(rs_b, b_off[i], smem + stage + (wave * SEG_B + i) * 1024);
+  };
+  // K tail: on the one partial step (K % 64 != 0) a chunk past K inside a
+  // valid row would read the start of the next row, so from that step on
+  // those chunks point out of range (every later step is out of range as a
+  // whole).  The offsets are masked once, not per load: a select feeding each
+  // load would sit in the MFMA stream and stall it.
+  const int tail = (K % BK) ? (K - 1) / BK : -1;
+  auto mask_tail = [&]() {
+    const int kr = K - tail * BK;
+#pragma unroll
+    for (int i = 0; i < SEG_A; ++i) a_off[i] = (a_chunk[i] * 8 < kr) ? a_off[i] : kOutOfRange;
+    if constexpr (!NN) {
+#pragma unroll
+      for (int i = 0; i < SEG_B; ++i) b_off[i] = (b_chunk[i] * 8 < kr) ? b_off[i] : kOutOfRange;
+    }
   };
 
   // ---- fragment reads -------------------------------------------------------
@@ -231,12 +242,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   const int KT = (K + BK - 1) / BK;
 
   // ---- prologue: A of steps 0, 1 and B of step 0 in flight; slice 0 read ----
+  if (tail == 0) mask_tail();
   prep_a(0);
 #pragma unroll
   for (int i = 0; i < SEG_A; ++i) load_a(a_base(0), i);
   prep_b(0);
 #pragma unroll
   for (int i = 0; i < SEG_B; ++i) load_b(b_base(0), i);
+  if (tail == 1) mask_tail();
   prep_a(1);
 #pragma unroll
   for (int i = 0; i < SEG_A; ++i) load_a(a_base(1), i);
@@ -252,6 +265,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
 
   // ---- main loop -------------------------------------------------------------
   for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 2 == tail) mask_tail();  // loads of steps kt+2 on are issued below
     const uint32_t ca = a_base(kt), cb = b_base(kt);
     const uint32_t na = a_base(kt + 1), nb = b_base(kt + 1);
     // X: slice 0; read slice 1; A of step kt+2 into the stage step kt-1 used

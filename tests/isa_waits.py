@@ -135,17 +135,20 @@ def check_kernel(lines) -> list:
 
 def loop_vmcnt_zero(lines) -> int:
     """Number of waits for every outstanding vector-memory operation inside
-    the kernel's innermost loops (lines between a loop header label and the
-    branch back to it)."""
-    count, header, inside = 0, None, False
-    for raw in lines:
+    the kernel's loops: the lines from a loop header label to the last
+    branch (conditional or not) back to it."""
+    count = 0
+    for h, raw in enumerate(lines):
         m = _LABEL.match(raw)
-        if m and "Loop Header" in raw:
-            header, inside = m.group(1), True
+        if not (m and "Loop Header" in raw):
             continue
-        s = raw.strip()
-        if inside and s.startswith("s_waitcnt") and "vmcnt(0)" in s:
-            count += 1
-        if inside and s.startswith("s_cbranch") and header and s.endswith(header):
-            inside = False
+        header = m.group(1)
+        back = [i for i, l in enumerate(lines) if i > h and "branch" in l.split(";")[0]
+                and l.split(";")[0].strip().endswith(header)]
+        if not back:
+            continue
+        for l in lines[h + 1:back[-1] + 1]:
+            s = l.split(";")[0].strip()
+            if s.startswith("s_waitcnt") and "vmcnt(0)" in s:
+                count += 1
     return count
