@@ -85,16 +85,27 @@ int find_kernel(int layout, int dtype, int bm) {
   return -1;
 }
 
-// Automatic choice: the largest square tile that still gives every CU
-// (256 of them) at least one workgroup; small problems take the small tiles.
+// Automatic choice: the tile size with the least estimated time, taken as
+// (waves of workgroups over the 256 CUs, one workgroup per CU) x (time of
+// one tile), a tile's time being its area over the per-CU throughput of that
+// tile size at full occupancy, measured relative to the 256 x 256 kernel
+// (128: 0.8, 64: 0.5).  Ties go to the larger tile.
 int auto_kernel(int layout, int dtype, int64_t M, int64_t N) {
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-  int bm;
-  if (t256 >= 256) bm = 256;
-  else if (t128 >= 128) bm = 128;
-  else bm = 64;
-  return find_kernel(layout, dtype, bm);
+  constexpr int64_t kCUs = 256;
+  const int sizes[3] = {256, 128, 64};
+  const int64_t rate10[3] = {10, 8, 5};  // relative throughput x 10
+  int best = 256;
+  int64_t best_cost = -1;
+  for (int i = 0; i < 3; ++i) {
+    const int64_t t = sizes[i];
+    const int64_t tiles = ((M + t - 1) / t) * ((N + t - 1) / t);
+    const int64_t cost = ((tiles + kCUs - 1) / kCUs) * t * t * 40 / rate10[i];
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = sizes[i];
+    }
+  }
+  return find_kernel(layout, dtype, best);
 }
 
 hgemm_status_t validate(int64_t M, int64_t N, int64_t K, int dtype, const void *A,

@@ -115,14 +115,21 @@ hgemm_status_t hgemm_nn_ex(int64_t M, int64_t N, int64_t K, int dtype,
 int hgemm_kernel_count(void);
 
 /* Description of kernel table entry `index` (NULL if out of range):
- * "<layout>_<dtype>_<BM>x<BN>x<BK>_<lds layout>".  The integers describing it
- * are written through the non-NULL pointers: layout 0 = TN, 1 = NN; dtype as
- * hgemm_dtype_t; the workgroup tile BM x BN x BK. */
+ * "<layout>_<dtype>_<BM>x<BN>x<BK>" for the production kernels (entries
+ * 0..11, the ones the automatic choice uses), with a suffix naming what an
+ * ablation changes ("_plainlds": LDS without the XOR swizzle, "_directepi":
+ * epilogue without LDS staging), and an "rs_" prefix for the register-staged
+ * 32x32x16 baseline design (suffix: its LDS layout).  The integers describing
+ * it are written through the non-NULL pointers: layout 0 = TN, 1 = NN; dtype
+ * as hgemm_dtype_t; the workgroup tile BM x BN x BK. */
 const char *hgemm_kernel_info(int index, int *layout, int *dtype, int *bm,
                               int *bn, int *bk);
 
 /* Kernel table index the automatic choice would use for this call (layout
- * 0 = TN, 1 = NN), or -1 for invalid arguments. */
+ * 0 = TN, 1 = NN), or -1 for invalid arguments.  The choice takes the tile
+ * size (256, 128 or 64, square) with the least estimated time: waves of
+ * workgroups over the 256 CUs times one tile's area over that tile size's
+ * relative throughput (1, 0.8, 0.5); ties go to the larger tile. */
 int hgemm_auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus
