@@ -76,6 +76,14 @@ def _load(mutation: int = 0) -> ctypes.CDLL:
     lib.oracle_hgemm_sampled.restype = ctypes.c_int
     lib.oracle_hgemm_f64.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, u16p, u16p, f64p]
     lib.oracle_hgemm_f64.restype = ctypes.c_int
+    dbl = ctypes.c_double
+    lib.oracle_gemm_rows.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64, dbl,
+                                     u16p, i64, u16p, i64, dbl, u16p, i64, u16p, i64, i64, i64]
+    lib.oracle_gemm_rows.restype = ctypes.c_int
+    lib.oracle_gemm_sampled.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                        dbl, u16p, i64, u16p, i64, dbl, u16p, i64, i64p, i64p,
+                                        i64, u16p]
+    lib.oracle_gemm_sampled.restype = ctypes.c_int
     lib.oracle_mutation.restype = ctypes.c_int
     _LIBS[mutation] = lib
     return lib
@@ -177,3 +185,64 @@ def hgemm_f64(layout, dtype, A: np.ndarray, B: np.ndarray, mutation: int = 0) ->
     if rc != 0:
         raise RuntimeError(f"oracle_hgemm_f64 failed with {rc}")
     return C
+
+
+# ------------------------------------------------------------------ general form
+def _gen_check(opA: int, opB: int, M: int, N: int, K: int, A, B, beta, Cin):
+    if opA not in (0, 1) or opB not in (0, 1):
+        raise ValueError("opA/opB must be 0 (as stored) or 1 (transposed)")
+    ra, ca = (M, K) if opA == 0 else (K, M)
+    rb, cb = (K, N) if opB == 0 else (N, K)
+    if A.ndim != 2 or A.shape[0] < ra or A.shape[1] < ca:
+        raise ValueError(f"A stored as {A.shape} cannot hold {ra} x {ca}")
+    if B.ndim != 2 or B.shape[0] < rb or B.shape[1] < cb:
+        raise ValueError(f"B stored as {B.shape} cannot hold {rb} x {cb}")
+    if beta != 0 and (Cin is None or Cin.ndim != 2 or Cin.shape[0] < M or Cin.shape[1] < N):
+        raise ValueError("beta != 0 needs Cin of at least M x N")
+
+
+def gemm(opA: int, opB: int, dtype, M: int, N: int, K: int, A: np.ndarray, B: np.ndarray,
+         alpha: float = 1.0, beta: float = 0.0, Cin: np.ndarray | None = None,
+         mutation: int = 0, rows: tuple[int, int] | None = None) -> np.ndarray:
+    """General form ``C = RNE(alpha * opA(A) opB(B) + beta * Cin)`` (uint16 bits, M x N).
+
+    A, B and Cin are 2-D uint16 arrays in their stored shape; the length of a
+    stored row is that operand's leading dimension (opA 0: A is M x K, 1: A is
+    stored K x M; opB 0: B is K x N, 1: B is stored N x K).  With beta == 0
+    Cin is not read.
+    """
+    A, B = _u16(A), _u16(B)
+    _gen_check(opA, opB, M, N, K, A, B, beta, Cin)
+    cin = _u16(Cin) if (Cin is not None and beta != 0) else None
+    C = np.zeros((M, N), dtype=np.uint16)
+    r0, r1 = rows if rows is not None else (0, M)
+    rc = _load(mutation).oracle_gemm_rows(
+        opA, opB, _code(_DTYPES, dtype), M, N, K, float(alpha), _ptr(A, ctypes.c_uint16),
+        A.shape[1], _ptr(B, ctypes.c_uint16), B.shape[1], float(beta),
+        _ptr(cin, ctypes.c_uint16) if cin is not None else None,
+        cin.shape[1] if cin is not None else 0, _ptr(C, ctypes.c_uint16), N, r0, r1)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_rows failed with {rc}")
+    return C
+
+
+def gemm_sampled(opA: int, opB: int, dtype, M: int, N: int, K: int, A: np.ndarray,
+                 B: np.ndarray, rows: np.ndarray, cols: np.ndarray, alpha: float = 1.0,
+                 beta: float = 0.0, Cin: np.ndarray | None = None,
+                 mutation: int = 0) -> np.ndarray:
+    """General form at (rows[i], cols[i]) (uint16 bits)."""
+    A, B = _u16(A), _u16(B)
+    _gen_check(opA, opB, M, N, K, A, B, beta, Cin)
+    cin = _u16(Cin) if (Cin is not None and beta != 0) else None
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    c = np.ascontiguousarray(cols, dtype=np.int64)
+    out = np.empty(r.shape, dtype=np.uint16)
+    rc = _load(mutation).oracle_gemm_sampled(
+        opA, opB, _code(_DTYPES, dtype), M, N, K, float(alpha), _ptr(A, ctypes.c_uint16),
+        A.shape[1], _ptr(B, ctypes.c_uint16), B.shape[1], float(beta),
+        _ptr(cin, ctypes.c_uint16) if cin is not None else None,
+        cin.shape[1] if cin is not None else 0, _ptr(r, ctypes.c_int64), _ptr(c, ctypes.c_int64),
+        r.size, _ptr(out, ctypes.c_uint16))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_sampled failed with {rc}")
+    return out

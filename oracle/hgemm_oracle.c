@@ -292,4 +292,121 @@ int oracle_hgemm_f64(int layout, int dtype, int64_t M, int64_t N, int64_t K,
   return 0;
 }
 
+/* ---------------------------------------------------------------------- */
+/* General form: operation flags, leading dimensions, alpha and beta.      */
+/*                                                                         */
+/*   C[m][n] = RNE( alpha * S[m][n] + beta * Cin[m][n] ),                  */
+/*   S[m][n] = sum_{k<K} opA(A)[m][k] * opB(B)[k][n]   (FP64, ascending k)  */
+/*                                                                         */
+/* Row-major storage throughout:                                           */
+/*   opA 0: A is M x K,        opA(A)[m][k] = A[m*lda + k]                  */
+/*   opA 1: A is stored K x M, opA(A)[m][k] = A[k*lda + m]                  */
+/*   opB 0: B is K x N,        opB(B)[k][n] = B[k*ldb + n]                  */
+/*   opB 1: B is stored N x K, opB(B)[k][n] = B[n*ldb + k]                  */
+/*   C and Cin are M x N with leading dimensions ldc and ldcin.            */
+/* The pages' two layouts are (opA, opB) = (0, 1) for TN and (0, 0) for    */
+/* NN with packed leading dimensions, alpha = 1 and beta = 0.  The pages   */
+/* stop at C = A*B; the alpha/beta update is the usual BLAS gemm one,      */
+/* beta == 0 meaning Cin is not read at all (it may hold NaN).             */
+/* ---------------------------------------------------------------------- */
+static inline uint16_t gen_a(int opA, const uint16_t *A, int64_t lda,
+                             int64_t m, int64_t k) {
+#if ORACLE_MUTATION == 8
+  /* planted mistake: a transposed A read as if it were not */
+  (void)opA;
+  return A[m * lda + k];
+#else
+  return opA ? A[k * lda + m] : A[m * lda + k];
+#endif
+}
+
+static inline uint16_t gen_b(int opB, const uint16_t *B, int64_t ldb, int64_t N,
+                             int64_t K, int64_t k, int64_t n) {
+#if ORACLE_MUTATION == 9
+  /* planted mistake: the leading dimension of B ignored (packed stride) */
+  (void)ldb;
+  return opB ? B[n * K + k] : B[k * N + n];
+#else
+  (void)N;
+  (void)K;
+  return opB ? B[n * ldb + k] : B[k * ldb + n];
+#endif
+}
+
+static double gen_element(int opA, int opB, const double *lut, int64_t N,
+                          int64_t K, double alpha, const uint16_t *A,
+                          int64_t lda, const uint16_t *B, int64_t ldb,
+                          double beta, const uint16_t *Cin, int64_t ldcin,
+                          int64_t m, int64_t n) {
+  double acc = 0.0;
+  for (int64_t k = 0; k < K; ++k)
+    acc += lut[gen_a(opA, A, lda, m, k)] * lut[gen_b(opB, B, ldb, N, K, k, n)];
+  double v = alpha * acc;
+#if ORACLE_MUTATION == 7
+  /* planted mistake: beta ignored */
+  (void)beta;
+  (void)Cin;
+  (void)ldcin;
+#else
+  if (beta != 0.0) v += beta * lut[Cin[m * ldcin + n]];
+#endif
+  return v;
+}
+
+static int check_gen(int opA, int opB, int dtype, int64_t M, int64_t N,
+                     int64_t K, int64_t lda, int64_t ldb, int64_t ldcin,
+                     double beta, const uint16_t *Cin) {
+  if ((opA != 0 && opA != 1) || (opB != 0 && opB != 1)) return -1;
+  if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+  if (M < 0 || N < 0 || K < 0) return -1;
+  if (lda < (opA ? M : K) || ldb < (opB ? K : N)) return -1;
+  if (beta != 0.0 && (Cin == NULL || ldcin < N)) return -1;
+  return 0;
+}
+
+/* Rows [row_begin, row_end) of the general form; C[m*ldc + n]. */
+int oracle_gemm_rows(int opA, int opB, int dtype, int64_t M, int64_t N,
+                     int64_t K, double alpha, const uint16_t *A, int64_t lda,
+                     const uint16_t *B, int64_t ldb, double beta,
+                     const uint16_t *Cin, int64_t ldcin, uint16_t *C,
+                     int64_t ldc, int64_t row_begin, int64_t row_end) {
+  if (check_gen(opA, opB, dtype, M, N, K, lda, ldb, ldcin, beta, Cin)) return -1;
+  if (ldc < N || row_begin < 0 || row_end > M || row_begin > row_end) return -1;
+  double *lut = make_lut(dtype);
+  if (!lut) return -2;
+  const fmt_t *f = fmt_of(dtype);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = row_begin; m < row_end; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      const double v = gen_element(opA, opB, lut, N, K, alpha, A, lda, B, ldb,
+                                   beta, Cin, ldcin, m, n);
+      C[m * ldc + n] = encode16(round_to_format(v, f), f);
+    }
+  free(lut);
+  return 0;
+}
+
+/* Selected elements of the general form: out[i] = C[rows[i]][cols[i]]. */
+int oracle_gemm_sampled(int opA, int opB, int dtype, int64_t M, int64_t N,
+                        int64_t K, double alpha, const uint16_t *A,
+                        int64_t lda, const uint16_t *B, int64_t ldb,
+                        double beta, const uint16_t *Cin, int64_t ldcin,
+                        const int64_t *rows, const int64_t *cols,
+                        int64_t count, uint16_t *out) {
+  if (check_gen(opA, opB, dtype, M, N, K, lda, ldb, ldcin, beta, Cin)) return -1;
+  for (int64_t i = 0; i < count; ++i)
+    if (rows[i] < 0 || rows[i] >= M || cols[i] < 0 || cols[i] >= N) return -1;
+  double *lut = make_lut(dtype);
+  if (!lut) return -2;
+  const fmt_t *f = fmt_of(dtype);
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t i = 0; i < count; ++i) {
+    const double v = gen_element(opA, opB, lut, N, K, alpha, A, lda, B, ldb,
+                                 beta, Cin, ldcin, rows[i], cols[i]);
+    out[i] = encode16(round_to_format(v, f), f);
+  }
+  free(lut);
+  return 0;
+}
+
 int oracle_mutation(void) { return ORACLE_MUTATION; }

@@ -357,9 +357,117 @@ def pin_golden(mutation: int = 0):
         same_bits(oracle.hgemm(layout, dt, A, B, mutation=mutation), want, f"golden {fn}")
 
 
+# --------------------------------------------------------------------------
+# General form: operation flags, leading dimensions, alpha and beta.
+# --------------------------------------------------------------------------
+_NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0}
+
+
+def _stored(logical: np.ndarray, transposed: bool, pad: int, fill: int) -> np.ndarray:
+    """Store a logical matrix (transposed or not) in a buffer whose rows are
+    `pad` elements longer than needed, the padding filled with `fill`."""
+    src = logical.T if transposed else logical
+    out = np.full((src.shape[0], src.shape[1] + pad), fill, dtype=np.uint16)
+    out[:, :src.shape[1]] = src
+    return out
+
+
+def exact_general(dtype, opA_log: np.ndarray, opB_log: np.ndarray, alpha, beta, Cin_log):
+    """Exact rational alpha * A B + beta * Cin on logical operands, rounded once."""
+    Av = [[Fraction(x) for x in row] for row in lib_decode(opA_log, dtype).tolist()]
+    Bc = [[Fraction(x) for x in col] for col in lib_decode(opB_log, dtype).T.tolist()]
+    Cv = lib_decode(Cin_log, dtype).tolist() if beta != 0 else None
+    g = grid(dtype)
+    al, be = Fraction(alpha), Fraction(beta)
+    out = np.zeros((len(Av), len(Bc)), dtype=np.uint16)
+    for m in range(len(Av)):
+        for n in range(len(Bc)):
+            v = al * sum((a * b for a, b in zip(Av[m], Bc[n])), Fraction(0))
+            if beta != 0:
+                v += be * Fraction(Cv[m][n])
+            out[m, n] = g.round(v)
+    return out
+
+
+GENERAL_CASES = [  # (M, N, K, alpha, beta)
+    (3, 5, 7, 1.0, 0.0), (6, 4, 9, -0.75, 0.0), (5, 6, 8, 1.5, 1.0), (7, 3, 5, 0.5, -0.25),
+    (1, 9, 16, 2.0, 3.0), (4, 4, 1, -1.0, 0.5),
+]
+
+
+def pin_general_bruteforce(mutation: int = 0):
+    """All four operation-flag combinations, padded leading dimensions and
+    dyadic alpha/beta, against exact rational arithmetic."""
+    for dt in ("f16", "bf16"):
+        for opA in (0, 1):
+            for opB in (0, 1):
+                for s, (M, N, K, al, be) in enumerate(GENERAL_CASES):
+                    A = inputs.draw((M, K), dt, "normal", 300 + s)
+                    Bl = inputs.draw((K, N), dt, "normal", 400 + s)
+                    Cin = inputs.draw((M, N), dt, "normal", 500 + s)
+                    want = exact_general(dt, A, Bl, al, be, Cin)
+                    As = _stored(A, opA == 1, 1 + s % 3, 0x3C00)
+                    Bs = _stored(Bl, opB == 1, 2 + s % 2, 0x3C00)
+                    Cs = _stored(Cin, False, 3, 0x3C00)
+                    got = oracle.gemm(opA, opB, dt, M, N, K, As, Bs, al, be, Cs, mutation=mutation)
+                    same_bits(got, want, f"general {dt} op{opA}{opB} {M}x{N}x{K} a={al} b={be}")
+
+
+def pin_general_small_integers(mutation: int = 0):
+    """C = 2 AB - Cin on small integers is exact in every format used: it
+    must equal the int64 result bit for bit, for every flag combination."""
+    g = np.random.Generator(np.random.PCG64(12))
+    for dt, hi, (M, N, K) in (("f16", 2, (9, 11, 128)), ("bf16", 1, (7, 13, 32))):
+        Ai = g.integers(-hi, hi + 1, size=(M, K))
+        Bi = g.integers(-hi, hi + 1, size=(K, N))
+        Ci = g.integers(-4, 5, size=(M, N))
+        want = _bits_of(2 * (Ai @ Bi) - Ci, dt)
+        for opA in (0, 1):
+            for opB in (0, 1):
+                As = _stored(_bits_of(Ai, dt), opA == 1, 8, 0)
+                Bs = _stored(_bits_of(Bi, dt), opB == 1, 16, 0)
+                got = oracle.gemm(opA, opB, dt, M, N, K, As, Bs, 2.0, -1.0,
+                                  _stored(_bits_of(Ci, dt), False, 8, 0), mutation=mutation)
+                same_bits(got, want, f"general integers {dt} op{opA}{opB}")
+
+
+def pin_general_padding_and_beta_zero(mutation: int = 0):
+    """NaN in the padding of every operand, and in C when beta == 0, must not
+    reach the result: it equals the packed, NaN-free computation."""
+    for dt in ("f16", "bf16"):
+        M, N, K = 6, 8, 10
+        A = inputs.draw((M, K), dt, "uniform", 61)
+        Bl = inputs.draw((K, N), dt, "uniform", 62)
+        ref = oracle.gemm(0, 0, dt, M, N, K, A, Bl, mutation=mutation)
+        nan = _NAN_BITS[dt]
+        for opA in (0, 1):
+            for opB in (0, 1):
+                As = _stored(A, opA == 1, 5, nan)
+                Bs = _stored(Bl, opB == 1, 7, nan)
+                Cs = np.full((M, N + 4), nan, dtype=np.uint16)
+                got = oracle.gemm(opA, opB, dt, M, N, K, As, Bs, 1.0, 0.0, Cs, mutation=mutation)
+                same_bits(got, ref, f"padding/beta=0 {dt} op{opA}{opB}")
+
+
+def pin_general_matches_layouts(mutation: int = 0):
+    """(opA, opB) = (0, 1) and (0, 0) with packed storage, alpha 1, beta 0 are
+    the TN and NN layouts, computed by the oracle's separately written loop."""
+    for dt in ("f16", "bf16"):
+        M, N, K = 13, 11, 37
+        A = inputs.draw((M, K), dt, "normal", 71)
+        Bt = inputs.draw((N, K), dt, "normal", 72)
+        same_bits(oracle.gemm(0, 1, dt, M, N, K, A, Bt, mutation=mutation),
+                  oracle.hgemm("tn", dt, A, Bt, mutation=mutation), f"general vs tn {dt}")
+        Bn = np.ascontiguousarray(Bt.T)
+        same_bits(oracle.gemm(0, 0, dt, M, N, K, A, Bn, mutation=mutation),
+                  oracle.hgemm("nn", dt, A, Bn, mutation=mutation), f"general vs nn {dt}")
+
+
 ALL_PINS = [
     pin_decode_exhaustive, pin_round_representable, pin_round_midpoints, pin_round_random,
     pin_round_special, pin_gemm_bruteforce, pin_gemm_small_integers,
     pin_gemm_identity_permutation, pin_gemm_closed_forms, pin_gemm_ties,
     pin_gemm_layout_invariants, pin_gemm_sampled_matches_full, pin_golden,
+    pin_general_bruteforce, pin_general_small_integers, pin_general_padding_and_beta_zero,
+    pin_general_matches_layouts,
 ]

@@ -17,7 +17,8 @@ def test_oracle_pin(pin):
 
 # Each planted mistake (a dropped k term, B read with the wrong layout, ties
 # rounded away from zero, truncation, a wrong bfloat16 exponent bias, a sign
-# error) must make at least one pin fail.
+# error, and in the general form: beta ignored, a transposed A read as
+# stored, B's leading dimension ignored) must make at least one pin fail.
 MUTATIONS = {
     1: "last k term dropped",
     2: "NN operand read as TN",
@@ -25,6 +26,9 @@ MUTATIONS = {
     4: "truncation instead of rounding",
     5: "wrong bf16 exponent bias",
     6: "sign error on odd k",
+    7: "general form ignores beta",
+    8: "general form reads a transposed A as stored",
+    9: "general form ignores the leading dimension of B",
 }
 
 
