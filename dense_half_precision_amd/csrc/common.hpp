@@ -20,15 +20,27 @@ namespace hgemm {
 // (eight-way).  The writes (8 lanes per row, all 8 chunks) stay conflict-free
 // under every layout.
 enum LdsLayout { kLdsXor = 0, kLdsPlain = 1, kLdsPad = 2, kLdsXorRow = 3 };
-enum Layout { kTN = 0, kNN = 1 };
+// Operand orientations (row-major storage).  Bit 0: B is stored K x N (n
+// contiguous) instead of N x K (k contiguous); bit 1: A is stored K x M (m
+// contiguous) instead of M x K.  TN and NN are the pages' two layouts.
+enum Layout {
+  kTN = 0,    // A[M][K], B stored as Bt[N][K]
+  kNN = 1,    // A[M][K], B[K][N]
+  kAtTN = 2,  // A stored as At[K][M], Bt[N][K]
+  kAtNN = 3,  // A stored as At[K][M], B[K][N]
+};
+constexpr bool a_mn_major(int layout) { return (layout & 2) != 0; }
+constexpr bool b_mn_major(int layout) { return (layout & 1) != 0; }
 
 struct GemmArgs {
   const uint16_t *A;
   const uint16_t *B;
   uint16_t *C;
   int M, N, K;
-  int group_m;   // >= 1
-  int xcd_remap; // 0 or 1
+  int lda, ldb, ldc;  // row strides (elements) of the stored A, B, C
+  float alpha, beta;  // C = alpha * A B + beta * C; beta == 0: C is not read
+  int group_m;        // >= 1
+  int xcd_remap;      // 0 or 1
 };
 
 // Scheduling hints for one phase: after each of the NMF matrix-core
@@ -53,8 +65,8 @@ __host__ __device__ __forceinline__ int chunk_pos(int r, int c) {
   else return c;
 }
 
-// NN operand B in LDS: k-rows of `row_bytes` (2*BN) bytes, n contiguous,
-// 16-byte chunks.  The transposing fragment read (lds_read_tr16) has the 16
+// An m- or n-contiguous operand in LDS (NN's B, a stored-transposed A): k-rows
+// of `row_bytes` (2*BN or 2*BM) bytes, 16-byte chunks.  The transposing fragment read (lds_read_tr16) has the 16
 // lanes of a group on k-rows 8g + 0..3 (and 8g + 4..7 for the second read),
 // four lanes per row on two adjacent chunks; with 256 bytes of banks a 512-
 // or 256-byte row maps every row onto the same banks, so the chunk is XORed

@@ -93,6 +93,18 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   }
 }
 
+// Packed pair of 16-bit values -> two FP32 values (exact).
+template <int DT>
+__device__ __forceinline__ void unpack2(uint32_t v, float &lo, float &hi) {
+  if constexpr (DT == kF16) {
+    lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+    hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+  } else {
+    lo = __builtin_bit_cast(float, v << 16);
+    hi = __builtin_bit_cast(float, v & 0xFFFF0000u);
+  }
+}
+
 // Buffer resource over [base, base + nbytes): 128-bit loads whose byte offset
 // is at or beyond nbytes return zero instead of touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t nbytes) {

@@ -76,8 +76,6 @@ struct TileCfg {
   static constexpr int LDS_BYTES = PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES;
   static constexpr int SEG_A = BM / 32;               // 1 KiB A segments per wave and step
   static constexpr int SEG_B = BN / 32;               // 1 KiB B segments per wave and step
-  static constexpr int NN_ROWB = BN * 2;              // NN: bytes per k-row of B in LDS
-  static constexpr int NN_CPR = BN / 8;               // NN: 16-byte chunks per k-row
   static_assert(BM % 64 == 0 && BN % 64 == 0 && BM <= 256 && BN <= 256, "tile");
   static_assert(FM % 2 == 0, "the slice is split in halves by A block");
   static_assert(LDS_BYTES <= 163840, "160 KiB of LDS");
@@ -89,98 +87,119 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
   constexpr int FM = T::FM, FN = T::FN, NMF = T::NMF;
   constexpr int SEG_A = T::SEG_A, SEG_B = T::SEG_B;
-  constexpr bool NN = LAYOUT == kNN;
-  constexpr int NRB = NN ? 2 * FN : FN;               // LDS reads for the B fragments of a slice
-  constexpr int NR = NRB + FM;                        // LDS reads per slice
+  constexpr bool A_MN = a_mn_major(LAYOUT);  // A stored K x M: transposing reads
+  constexpr bool B_MN = b_mn_major(LAYOUT);  // B stored K x N: transposing reads
+  constexpr int NRA = A_MN ? 2 * FM : FM;    // LDS reads for the A fragments of a slice
+  constexpr int NRB = B_MN ? 2 * FN : FN;    // ... and for the B fragments
+  constexpr int NR = NRA + NRB;              // LDS reads per slice
+  // Read order within a slice: the transposing reads (inline assembly, not
+  // tracked by the compiler's wait-count pass) go first, so that the wait the
+  // compiler places for a later, tracked read of the same slice also covers
+  // them (LDS reads complete in order).  With both operands transposed there
+  // is no tracked read, and an explicit wait opens each slice instead.
+  constexpr bool A_FIRST = A_MN && !B_MN;
+  constexpr bool ALL_TR = A_MN && B_MN;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
 
   const int M = args.M, N = args.N, K = args.K;
+  const int lda = args.lda, ldb = args.ldb;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, args.group_m, args.xcd_remap, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  // tile_coords divides on the vector unit; the tile origin is uniform and is
+  // moved to scalar registers explicitly, so that the buffer descriptors built
+  // from it stay scalar (a descriptor held in vector registers turns every
+  // load into a per-lane loop)
+  const int m0 = __builtin_amdgcn_readfirstlane(tm * BM);
+  const int n0 = __builtin_amdgcn_readfirstlane(tn * BN);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
 
   // ---- direct-to-LDS loads ------------------------------------------------
-  // A (and TN B): segment s = 8 tile rows of 128 bytes; lane -> (row s*8 +
-  // lane/8, stored chunk lane%8), which holds logical k-chunk
-  // (lane%8) ^ swizzle(row).  Wave w loads segments w*SEG .. w*SEG+SEG-1.
+  // k-contiguous operand (A[M][K], Bt[N][K]): segment s = 8 tile rows of 128
+  // bytes; lane -> (row s*8 + lane/8, stored chunk lane%8), which holds logical
+  // k-chunk (lane%8) ^ swizzle(row).
+  // m/n-contiguous operand (At[K][M], B[K][N]): segment s = RPS k-rows of
+  // 2*BX bytes; lane -> (k-row s*RPS + lane/CPR, stored chunk lane%CPR) holding
+  // m/n-chunk (lane%CPR) ^ nn_chunk_xor(k); chunks past the M/N edge (a
+  // multiple of 8) read out of range.
+  // Wave w loads segments w*SEG .. w*SEG+SEG-1 of each operand.
   const int seg_row = lane >> 3, pchunk = lane & 7;
+  auto kmaj_off = [&](int seg, int ld, int &chunk) {
+    const int row = seg * 8 + seg_row;
+    chunk = pchunk ^ (chunk_pos<T::LDS>(row, 0));
+    return (uint32_t)(row * ld + chunk * 8) * 2u;
+  };
+  auto mnmaj_off = [&](int seg, int ld, int rowb, int x0, int xdim, int &chunk) {
+    const int cpr = rowb / 16, rps = 1024 / rowb;
+    const int k = seg * rps + lane / cpr;
+    const int c = (lane % cpr) ^ nn_chunk_xor<T::LDS>(k, rowb);
+    chunk = c;
+    return (x0 + c * 8 < xdim) ? (uint32_t)(k * ld + c * 8) * 2u : kOutOfRange;
+  };
   uint32_t a_off[SEG_A];
   int a_chunk[SEG_A];
 #pragma unroll
-  for (int i = 0; i < SEG_A; ++i) {
-    const int row = (wave * SEG_A + i) * 8 + seg_row;
-    a_chunk[i] = pchunk ^ (chunk_pos<T::LDS>(row, 0));
-    a_off[i] = (uint32_t)(row * K + a_chunk[i] * 8) * 2u;
-  }
+  for (int i = 0; i < SEG_A; ++i)
+    a_off[i] = A_MN ? mnmaj_off(wave * SEG_A + i, lda, 2 * BM, m0, M, a_chunk[i])
+                    : kmaj_off(wave * SEG_A + i, lda, a_chunk[i]);
   uint32_t b_off[SEG_B];
   int b_chunk[SEG_B];
-  // NN B: segment s = RPS k-rows of 2*BN bytes; lane -> (k-row s*RPS + lane/CPR,
-  // stored chunk lane%CPR) holding n-chunk (lane%CPR) ^ nn_chunk_xor(k).
-  constexpr int RPS = 1024 / T::NN_ROWB;
 #pragma unroll
-  for (int i = 0; i < SEG_B; ++i) {
-    if constexpr (!NN) {
-      const int row = (wave * SEG_B + i) * 8 + seg_row;
-      b_chunk[i] = pchunk ^ (chunk_pos<T::LDS>(row, 0));
-      b_off[i] = (uint32_t)(row * K + b_chunk[i] * 8) * 2u;
-    } else {
-      const int k = (wave * SEG_B + i) * RPS + lane / T::NN_CPR;
-      const int c = (lane % T::NN_CPR) ^ nn_chunk_xor<T::LDS>(k, T::NN_ROWB);
-      b_chunk[i] = c;
-      b_off[i] = (n0 + c * 8 < N) ? (uint32_t)(k * N + c * 8) * 2u : kOutOfRange;
-    }
-  }
-  const uint16_t *a_panel = args.A + (size_t)m0 * K;
-  const uint16_t *b_panel = NN ? args.B + n0 : args.B + (size_t)n0 * K;
+  for (int i = 0; i < SEG_B; ++i)
+    b_off[i] = B_MN ? mnmaj_off(wave * SEG_B + i, ldb, 2 * BN, n0, N, b_chunk[i])
+                    : kmaj_off(wave * SEG_B + i, ldb, b_chunk[i]);
+  const uint16_t *a_panel = A_MN ? args.A + m0 : args.A + (size_t)m0 * lda;
+  const uint16_t *b_panel = B_MN ? args.B + n0 : args.B + (size_t)n0 * ldb;
 
   // A stage of step s at (s % 3) * A_STAGE, B stage at B_BASE + (s & 1) * B_STAGE
   auto a_base = [&](int s) { return (uint32_t)((s % 3) * T::A_STAGE); };
   auto b_base = [&](int s) { return (uint32_t)(T::B_BASE + (s & 1) * T::B_STAGE); };
 
+  // Buffer resource of one operand for the K step starting at k0: rows past
+  // the tile edge (k-contiguous) or k-rows past K (m/n-contiguous) fall
+  // outside it and read as zero.
+  // (One descriptor built from selected base and size: descriptors merged from
+  // branches lose their uniformity and end up in a per-lane loop.)
+  auto rsrc_of = [&](bool mn, const uint16_t *panel, int ld, int rows, int k0) {
+    const int krem = K - k0;
+    const uint16_t *base = mn ? panel + (size_t)k0 * ld : panel + k0;
+    const uint32_t bytes = krem <= 0 ? 0u
+                           : mn      ? (uint32_t)(min(krem, BK) * ld) * 2u
+                                     : (uint32_t)((rows - 1) * ld + K - k0) * 2u;
+    return make_rsrc(base, bytes);
+  };
   __amdgpu_buffer_rsrc_t rs_a, rs_b;
-  int krem_a = 0, krem_b = 0;
-  auto prep_a = [&](int step) {
-    const int k0 = step * BK;
-    krem_a = K - k0;
-    rs_a = make_rsrc(a_panel + k0, krem_a > 0 ? (uint32_t)(rows_a * K - k0) * 2u : 0u);
-  };
-  auto prep_b = [&](int step) {
-    const int k0 = step * BK;
-    krem_b = K - k0;
-    if constexpr (!NN)
-      rs_b = make_rsrc(b_panel + k0, krem_b > 0 ? (uint32_t)(rows_b * K - k0) * 2u : 0u);
-    else  // k-rows k0 .. k0+63 of B[K][N]; rows past K fall outside
-      rs_b = make_rsrc(b_panel + (size_t)k0 * N, krem_b > 0 ? (uint32_t)(min(krem_b, BK) * N) * 2u : 0u);
-  };
+  auto prep_a = [&](int step) { rs_a = rsrc_of(A_MN, a_panel, lda, rows_a, step * BK); };
+  auto prep_b = [&](int step) { rs_b = rsrc_of(B_MN, b_panel, ldb, rows_b, step * BK); };
   auto load_a = [&](uint32_t stage, int i) {
     load16_lds(rs_a, a_off[i], smem + stage + (wave * SEG_A + i) * 1024);
   };
   auto load_b = [&](uint32_t stage, int i) {
     load16_lds(rs_b, b_off[i], smem + stage + (wave * SEG_B + i) * 1024);
   };
-  // K tail: on the one partial step (K % 64 != 0) a chunk past K inside a
-  // valid row would read the start of the next row, so from that step on
-  // those chunks point out of range (every later step is out of range as a
-  // whole).  The offsets are masked once, not per load: a select feeding each
-  // load would sit in the MFMA stream and stall it.
+  // K tail: on the one partial step (K % 64 != 0) a k-chunk past K inside a
+  // valid row of a k-contiguous operand would read past the row's end, so from
+  // that step on those chunks point out of range (every later step is out of
+  // range as a whole).  The offsets are masked once, not per load: a select
+  // feeding each load would sit in the MFMA stream and stall it.
   const int tail = (K % BK) ? (K - 1) / BK : -1;
   auto mask_tail = [&]() {
     const int kr = K - tail * BK;
+    if constexpr (!A_MN) {
 #pragma unroll
-    for (int i = 0; i < SEG_A; ++i) a_off[i] = (a_chunk[i] * 8 < kr) ? a_off[i] : kOutOfRange;
-    if constexpr (!NN) {
+      for (int i = 0; i < SEG_A; ++i) a_off[i] = (a_chunk[i] * 8 < kr) ? a_off[i] : kOutOfRange;
+    }
+    if constexpr (!B_MN) {
 #pragma unroll
       for (int i = 0; i < SEG_B; ++i) b_off[i] = (b_chunk[i] * 8 < kr) ? b_off[i] : kOutOfRange;
     }
   };
 
   // ---- fragment reads -------------------------------------------------------
-  // A / TN B: 16 rows x 32 k; lane reads row (lane & 15), logical k-chunk
+  // k-contiguous: 16 rows x 32 k; lane reads row (lane & 15), logical k-chunk
   // 4*slice + lane/16 of that row.
   uint32_t rd_off[2];
 #pragma unroll
@@ -188,39 +207,65 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
     rd_off[sl] = (lane & 15) * 128 + chunk_pos<T::LDS>(lane & 15, 4 * sl + (lane >> 4)) * 16;
   const uint32_t rd_a = (wm * T::WTM) * 128;
   const uint32_t rd_b = (wn * T::WTN) * 128;
-  // NN B: lane i of group g points at k-row 8g + i/4 (+4 for the second read)
-  // of slice sl, n = 16j + 4*(i%4) .. +3 of the wave's columns.
-  uint32_t tr_off[NN ? FN : 1];
-  if constexpr (NN) {
+  // m/n-contiguous: lane i of group g points at k-row 8g + i/4 (+4 for the
+  // second read) of slice sl, m/n = 16j + 4*(i%4) .. +3 of the wave's block.
+  auto tr_offsets = [&](uint32_t *off, int nfrag, int x_wave, int rowb) {
     const int g = lane >> 4, i = lane & 15;
     const int k = 8 * g + (i >> 2);
-    const int fx = nn_chunk_xor<T::LDS>(k, T::NN_ROWB);
+    const int fx = nn_chunk_xor<T::LDS>(k, rowb);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int cbase = (wn * T::WTN + 16 * j) / 8;  // even chunk index
+    for (int j = 0; j < nfrag; ++j) {
+      const int cbase = (x_wave + 16 * j) / 8;  // even chunk index
       const int c = (cbase ^ fx) + ((i & 3) >> 1);
-      tr_off[j] = k * T::NN_ROWB + c * 16 + (i & 1) * 8;
+      off[j] = k * rowb + c * 16 + (i & 1) * 8;
     }
-  }
+  };
+  uint32_t tra_off[A_MN ? FM : 1], trb_off[B_MN ? FN : 1];
+  if constexpr (A_MN) tr_offsets(tra_off, FM, wm * T::WTM, 2 * BM);
+  if constexpr (B_MN) tr_offsets(trb_off, FN, wn * T::WTN, 2 * BN);
 
   u32x4 f[2][FN + FM];  // [set][B fragments 0..FN-1, A fragments FN..FN+FM-1]
-  // read op q (0..NR-1) of slice sl into set S: B fragments first, then A
-  auto read_op = [&](auto S_, uint32_t ab, uint32_t bb, int sl, int q) {
+  auto read_a = [&](auto S_, uint32_t ab, int sl, int qa) {
     constexpr int S = decltype(S_)::value;
-    if (q < NRB) {
-      if constexpr (!NN) {
-        f[S][q] = *(const u32x4 *)(smem + bb + rd_b + q * 16 * 128 + rd_off[sl]);
-      } else {
-        const int j = q >> 1, h = q & 1;
-        // every MFMA that takes this B fragment also takes an A fragment of the
-        // same slice, read below (q >= NRB): its wait covers this read
-        const u32x2 v = lds_read_tr16(lds_addr(smem + bb + tr_off[j]), (32 * sl + 4 * h) * T::NN_ROWB);
-        f[S][j][2 * h] = v[0];
-        f[S][j][2 * h + 1] = v[1];
-      }
+    if constexpr (A_MN) {
+      const int i = qa >> 1, h = qa & 1;
+      const u32x2 v = lds_read_tr16(lds_addr(smem + ab + tra_off[i]), (32 * sl + 4 * h) * 2 * BM);
+      f[S][FN + i][2 * h] = v[0];
+      f[S][FN + i][2 * h + 1] = v[1];
     } else {
-      const int i = q - NRB;
-      f[S][FN + i] = *(const u32x4 *)(smem + ab + rd_a + i * 16 * 128 + rd_off[sl]);
+      f[S][FN + qa] = *(const u32x4 *)(smem + ab + rd_a + qa * 16 * 128 + rd_off[sl]);
+    }
+  };
+  auto read_b = [&](auto S_, uint32_t bb, int sl, int qb) {
+    constexpr int S = decltype(S_)::value;
+    if constexpr (B_MN) {
+      const int j = qb >> 1, h = qb & 1;
+      const u32x2 v = lds_read_tr16(lds_addr(smem + bb + trb_off[j]), (32 * sl + 4 * h) * 2 * BN);
+      f[S][j][2 * h] = v[0];
+      f[S][j][2 * h + 1] = v[1];
+    } else {
+      f[S][qb] = *(const u32x4 *)(smem + bb + rd_b + qb * 16 * 128 + rd_off[sl]);
+    }
+  };
+  // read op q (0..NR-1) of slice sl into set S, in the order stated above
+  auto read_op = [&](auto S_, uint32_t ab, uint32_t bb, int sl, int q) {
+    if constexpr (A_FIRST) {
+      if (q < NRA) read_a(S_, ab, sl, q);
+      else read_b(S_, bb, sl, q - NRA);
+    } else {
+      if (q < NRB) read_b(S_, bb, sl, q);
+      else read_a(S_, ab, sl, q - NRB);
+    }
+  };
+  // With no tracked read in a slice: wait for all of its reads before its
+  // first MFMA, the fragment registers tied to the wait so that neither an
+  // MFMA nor another value can use them earlier.
+  auto wait_set = [&](auto S_) {
+    constexpr int S = decltype(S_)::value;
+    if constexpr (ALL_TR) {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[S][0]));
+#pragma unroll
+      for (int q = 1; q < FN + FM; ++q) asm volatile("" : "+v"(f[S][q]));
     }
   };
 
@@ -271,6 +316,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
     // X: slice 0; read slice 1; A of step kt+2 into the stage step kt-1 used
     prep_a(kt + 2);
     const uint32_t la = a_base(kt + 2);
+    wait_set(I0{});
 #pragma unroll
     for (int t = 0; t < NMF; ++t) {
       mfma(I0{}, t);
@@ -283,6 +329,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
       __builtin_amdgcn_sched_barrier(0);
     }
     // Y: first half of slice 1
+    wait_set(I1{});
 #pragma unroll
     for (int t = 0; t < NMF / 2; ++t) {
       mfma(I1{}, t);
@@ -312,59 +359,95 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   // The last step (or, for K = 0, the prologue) read fragments for a step that
   // does not exist; the compiler sees those values dead and may hand their
   // registers to the epilogue while the transposing reads, which it does not
-  // track, still write them.  Wait for them here, and keep the B fragment
+  // track, still write them.  Wait for them here, and keep the fragment
   // registers alive up to the wait.
-  if constexpr (NN) {
+  if constexpr (A_MN || B_MN) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0][0]));
 #pragma unroll
-    for (int j = 1; j < FN; ++j) asm volatile("" : "+v"(f[0][j]));
+    for (int q = 1; q < FN + FM; ++q) asm volatile("" : "+v"(f[0][q]));
   }
 
   // ---- epilogue --------------------------------------------------------------
   // lane holds, for tile (i, j): C[m][n .. n+3], m = wave row + 16i + lane%16,
-  // n = wave column + 16j + 4*(lane/16)
+  // n = wave column + 16j + 4*(lane/16).  C = alpha * acc + beta * C, rounded
+  // once to the output type; with alpha == 1 and beta == 0 the FP32 sums are
+  // converted as they are and C is not read.
+  const int ldc = args.ldc;
   const int wm0 = m0 + wm * T::WTM, wn0 = n0 + wn * T::WTN;
-  if constexpr (T::EPI) {
-    __builtin_amdgcn_s_waitcnt(0);  // no load still writing LDS, no read pending
-    wg_barrier();                   // every wave is done with the pipeline stages
-    char *cw = smem + wave * (T::WTM * T::CROW);
+  const float alpha = args.alpha, beta = args.beta;
+  // packed output of tile (i, j) for this lane
+  auto out2 = [&](auto GEN_, int i, int j) {
+    constexpr bool GEN = decltype(GEN_)::value;
+    float x[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+    if constexpr (GEN) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        u32x2 v;
-        v[0] = pack2<DT>(acc[i][j][0], acc[i][j][1]);
-        v[1] = pack2<DT>(acc[i][j][2], acc[i][j][3]);
-        *(u32x2 *)(cw + (i * 16 + (lane & 15)) * T::CROW + (j * 16 + 4 * (lane >> 4)) * 2) = v;
-      }
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-    // each row of the wave block is WTN*2 bytes = WTN/8 lanes of 16 bytes
-    constexpr int LPR = T::WTN / 8, RPI = 64 / LPR;
-#pragma unroll
-    for (int r = 0; r < T::WTM / RPI; ++r) {
-      const int row = r * RPI + lane / LPR, col = 8 * (lane % LPR);
-      const u32x4 v = *(const u32x4 *)(cw + row * T::CROW + col * 2);
-      const int m = wm0 + row, n = wn0 + col;
-      if (m < M && n < N) *(u32x4 *)(args.C + (size_t)m * N + n) = v;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = wm0 + i * 16 + (lane & 15);
-      if (m >= M) continue;
-      uint16_t *crow = args.C + (size_t)m * N;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = wn0 + j * 16 + 4 * (lane >> 4);
-        if (n < N) {
-          u32x2 v;
-          v[0] = pack2<DT>(acc[i][j][0], acc[i][j][1]);
-          v[1] = pack2<DT>(acc[i][j][2], acc[i][j][3]);
-          *(u32x2 *)(crow + n) = v;
+      for (int e = 0; e < 4; ++e) x[e] *= alpha;
+      if (beta != 0.0f) {
+        const int m = wm0 + i * 16 + (lane & 15), n = wn0 + j * 16 + 4 * (lane >> 4);
+        if (m < M && n < N) {
+          const u32x2 c = *(const u32x2 *)(args.C + (size_t)m * ldc + n);
+          float c0, c1, c2, c3;
+          unpack2<DT>(c[0], c0, c1);
+          unpack2<DT>(c[1], c2, c3);
+          x[0] = __builtin_fmaf(beta, c0, x[0]);
+          x[1] = __builtin_fmaf(beta, c1, x[1]);
+          x[2] = __builtin_fmaf(beta, c2, x[2]);
+          x[3] = __builtin_fmaf(beta, c3, x[3]);
         }
       }
     }
-  }
+    u32x2 v;
+    v[0] = pack2<DT>(x[0], x[1]);
+    v[1] = pack2<DT>(x[2], x[3]);
+    return v;
+  };
+  // In the general form the reads of the old C go one row block at a time
+  // (the empty asm keeps later rows' reads from being hoisted), so that their
+  // registers do not pile up next to the accumulators.
+  auto epilogue = [&](auto GEN_) {
+    constexpr bool GEN = decltype(GEN_)::value;
+    if constexpr (T::EPI) {
+      __builtin_amdgcn_s_waitcnt(0);  // no load still writing LDS, no read pending
+      wg_barrier();                   // every wave is done with the pipeline stages
+      char *cw = smem + wave * (T::WTM * T::CROW);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          *(u32x2 *)(cw + (i * 16 + (lane & 15)) * T::CROW + (j * 16 + 4 * (lane >> 4)) * 2) =
+              out2(GEN_, i, j);
+        if constexpr (GEN) asm volatile("" ::: "memory");
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+      // each row of the wave block is WTN*2 bytes = WTN/8 lanes of 16 bytes
+      constexpr int LPR = T::WTN / 8, RPI = 64 / LPR;
+#pragma unroll
+      for (int r = 0; r < T::WTM / RPI; ++r) {
+        const int row = r * RPI + lane / LPR, col = 8 * (lane % LPR);
+        const u32x4 v = *(const u32x4 *)(cw + row * T::CROW + col * 2);
+        const int m = wm0 + row, n = wn0 + col;
+        if (m < M && n < N) *(u32x4 *)(args.C + (size_t)m * ldc + n) = v;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = wm0 + i * 16 + (lane & 15);
+        if (m < M) {
+          uint16_t *crow = args.C + (size_t)m * ldc;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int n = wn0 + j * 16 + 4 * (lane >> 4);
+            if (n < N) *(u32x2 *)(crow + n) = out2(GEN_, i, j);
+          }
+        }
+        if constexpr (GEN) asm volatile("" ::: "memory");
+      }
+    }
+  };
+  if (alpha == 1.0f && beta == 0.0f)
+    epilogue(std::false_type{});
+  else
+    epilogue(std::true_type{});
 }
 
 }  // namespace hgemm

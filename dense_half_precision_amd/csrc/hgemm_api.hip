@@ -21,17 +21,20 @@ typedef void (*kernel_fn)(GemmArgs);
 struct KernelEntry {
   const char *name;
   int layout, dtype, bm, bn, bk, lds, default_group_m;
+  bool production;  // candidate of the automatic choice
+  bool general;     // honours leading dimensions, alpha and beta
   kernel_fn fn;
 };
 
 template <class T, int LAYOUT, int DT>
-constexpr KernelEntry entry(const char *name, int group_m) {
-  return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m,
+constexpr KernelEntry entry(const char *name, int group_m, bool production) {
+  return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, production, true,
                      &gemm_kernel<T, LAYOUT, DT>};
 }
+// the register-staged baseline assumes packed TN/NN operands, alpha 1, beta 0
 template <class T, int LAYOUT, int DT>
 constexpr KernelEntry rs_entry(const char *name, int group_m) {
-  return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m,
+  return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, false, false,
                      &regstage_kernel<T, LAYOUT, DT>};
 }
 
@@ -45,43 +48,62 @@ using R256Plain = RsCfg<256, 256, 2, 2, kLdsPlain>;
 using R256Pad = RsCfg<256, 256, 2, 2, kLdsPad>;
 using R256XorRow = RsCfg<256, 256, 2, 2, kLdsXorRow>;
 
-// Index order is part of the ablation interface (hgemm_kernel_info lists it).
-// Entries 0..11 are the production kernels the automatic choice picks from.
+// Index order is part of the ablation interface (hgemm_kernel_info lists it);
+// new entries are appended.
 const KernelEntry kTable[] = {
-    entry<T256, kTN, kF16>("tn_f16_256x256x64", 4),
-    entry<T256, kTN, kBF16>("tn_bf16_256x256x64", 4),
-    entry<T256, kNN, kF16>("nn_f16_256x256x64", 4),
-    entry<T256, kNN, kBF16>("nn_bf16_256x256x64", 4),
-    entry<T128, kTN, kF16>("tn_f16_128x128x64", 4),
-    entry<T128, kTN, kBF16>("tn_bf16_128x128x64", 4),
-    entry<T128, kNN, kF16>("nn_f16_128x128x64", 4),
-    entry<T128, kNN, kBF16>("nn_bf16_128x128x64", 4),
-    entry<T64, kTN, kF16>("tn_f16_64x64x64", 4),
-    entry<T64, kTN, kBF16>("tn_bf16_64x64x64", 4),
-    entry<T64, kNN, kF16>("nn_f16_64x64x64", 4),
-    entry<T64, kNN, kBF16>("nn_bf16_64x64x64", 4),
+    entry<T256, kTN, kF16>("tn_f16_256x256x64", 4, true),
+    entry<T256, kTN, kBF16>("tn_bf16_256x256x64", 4, true),
+    entry<T256, kNN, kF16>("nn_f16_256x256x64", 4, true),
+    entry<T256, kNN, kBF16>("nn_bf16_256x256x64", 4, true),
+    entry<T128, kTN, kF16>("tn_f16_128x128x64", 4, true),
+    entry<T128, kTN, kBF16>("tn_bf16_128x128x64", 4, true),
+    entry<T128, kNN, kF16>("nn_f16_128x128x64", 4, true),
+    entry<T128, kNN, kBF16>("nn_bf16_128x128x64", 4, true),
+    entry<T64, kTN, kF16>("tn_f16_64x64x64", 4, true),
+    entry<T64, kTN, kBF16>("tn_bf16_64x64x64", 4, true),
+    entry<T64, kNN, kF16>("nn_f16_64x64x64", 4, true),
+    entry<T64, kNN, kBF16>("nn_bf16_64x64x64", 4, true),
     // ablations of the production kernel: unswizzled LDS, direct epilogue stores
-    entry<T256Plain, kTN, kF16>("tn_f16_256x256x64_plainlds", 4),
-    entry<T256Plain, kNN, kBF16>("nn_bf16_256x256x64_plainlds", 4),
-    entry<T256Direct, kTN, kF16>("tn_f16_256x256x64_directepi", 4),
+    entry<T256Plain, kTN, kF16>("tn_f16_256x256x64_plainlds", 4, false),
+    entry<T256Plain, kNN, kBF16>("nn_bf16_256x256x64_plainlds", 4, false),
+    entry<T256Direct, kTN, kF16>("tn_f16_256x256x64_directepi", 4, false),
     // baseline design: register-staged loads, 32x32x16 MFMA, LDS layout variants
     rs_entry<R256, kTN, kF16>("rs_tn_f16_256x256x64_xor", 8),
     rs_entry<R256Plain, kTN, kF16>("rs_tn_f16_256x256x64_plain", 8),
     rs_entry<R256Pad, kTN, kF16>("rs_tn_f16_256x256x64_pad", 8),
     rs_entry<R256XorRow, kTN, kF16>("rs_tn_f16_256x256x64_xorrow", 8),
     rs_entry<R256, kNN, kBF16>("rs_nn_bf16_256x256x64_xor", 8),
+    // A stored transposed (At[K][M]) with Bt[N][K] or B[K][N]
+    entry<T256, kAtTN, kF16>("at_tn_f16_256x256x64", 4, true),
+    entry<T256, kAtTN, kBF16>("at_tn_bf16_256x256x64", 4, true),
+    entry<T256, kAtNN, kF16>("at_nn_f16_256x256x64", 4, true),
+    entry<T256, kAtNN, kBF16>("at_nn_bf16_256x256x64", 4, true),
+    entry<T128, kAtTN, kF16>("at_tn_f16_128x128x64", 4, true),
+    entry<T128, kAtTN, kBF16>("at_tn_bf16_128x128x64", 4, true),
+    entry<T128, kAtNN, kF16>("at_nn_f16_128x128x64", 4, true),
+    entry<T128, kAtNN, kBF16>("at_nn_bf16_128x128x64", 4, true),
+    entry<T64, kAtTN, kF16>("at_tn_f16_64x64x64", 4, true),
+    entry<T64, kAtTN, kBF16>("at_tn_bf16_64x64x64", 4, true),
+    entry<T64, kAtNN, kF16>("at_nn_f16_64x64x64", 4, true),
+    entry<T64, kAtNN, kBF16>("at_nn_bf16_64x64x64", 4, true),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
 constexpr int64_t kMaxM = int64_t(1) << 30;
 constexpr int64_t kMaxN = int64_t(1) << 23;
 constexpr int64_t kMaxK = int64_t(1) << 21;
-
-constexpr int kProductionKernels = 12;
+// leading dimensions: a k-contiguous operand (A[M][K], Bt[N][K]) is addressed
+// 256 rows at a time with 32-bit byte offsets; an m/n-contiguous one (At[K][M],
+// B[K][N]) 64 k-rows at a time; C with 64-bit offsets
+constexpr int64_t kMaxLdK = int64_t(1) << 22;
+constexpr int64_t kMaxLdMN = int64_t(1) << 23;
+constexpr int64_t kMaxLdC = (int64_t(1) << 31) - 8;
 
 int find_kernel(int layout, int dtype, int bm) {
-  for (int i = 0; i < kProductionKernels; ++i)
-    if (kTable[i].layout == layout && kTable[i].dtype == dtype && kTable[i].bm == bm) return i;
+  for (int i = 0; i < kTableSize; ++i)
+    if (kTable[i].production && kTable[i].layout == layout && kTable[i].dtype == dtype &&
+        kTable[i].bm == bm)
+      return i;
   return -1;
 }
 
@@ -108,24 +130,40 @@ int auto_kernel(int layout, int dtype, int64_t M, int64_t N) {
   return find_kernel(layout, dtype, best);
 }
 
-hgemm_status_t validate(int64_t M, int64_t N, int64_t K, int dtype, const void *A,
-                        const void *B, const void *C) {
-  if (M < 0 || N < 0 || K < 0) return HGEMM_ERR_INVALID_ARG;
-  if (dtype != HGEMM_F16 && dtype != HGEMM_BF16) return HGEMM_ERR_INVALID_ARG;
-  if (M == 0 || N == 0) return HGEMM_OK;
-  if (C == nullptr) return HGEMM_ERR_INVALID_ARG;
-  if (K > 0 && (A == nullptr || B == nullptr)) return HGEMM_ERR_INVALID_ARG;
-  if (N % 8 != 0 || K % 8 != 0) return HGEMM_ERR_UNSUPPORTED;
-  if (M > kMaxM || N > kMaxN || K > kMaxK) return HGEMM_ERR_UNSUPPORTED;
-  if ((reinterpret_cast<uintptr_t>(C) & 15) != 0) return HGEMM_ERR_UNSUPPORTED;
-  if (K > 0 && (((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) != 0))
+struct Call {
+  int layout;  // kTN, kNN, kAtTN, kAtNN
+  int64_t M, N, K;
+  int dtype;
+  float alpha, beta;
+  const void *A, *B;
+  void *C;
+  int64_t lda, ldb, ldc;
+};
+
+hgemm_status_t validate(const Call &c) {
+  if (c.M < 0 || c.N < 0 || c.K < 0) return HGEMM_ERR_INVALID_ARG;
+  if (c.dtype != HGEMM_F16 && c.dtype != HGEMM_BF16) return HGEMM_ERR_INVALID_ARG;
+  const bool a_mn = a_mn_major(c.layout), b_mn = b_mn_major(c.layout);
+  if (c.lda < (a_mn ? c.M : c.K) || c.ldb < (b_mn ? c.N : c.K) || c.ldc < c.N)
+    return HGEMM_ERR_INVALID_ARG;
+  if (c.M == 0 || c.N == 0) return HGEMM_OK;
+  if (c.C == nullptr) return HGEMM_ERR_INVALID_ARG;
+  if (c.K > 0 && (c.A == nullptr || c.B == nullptr)) return HGEMM_ERR_INVALID_ARG;
+  if (c.N % 8 != 0 || c.K % 8 != 0 || (a_mn && c.M % 8 != 0)) return HGEMM_ERR_UNSUPPORTED;
+  if (c.lda % 8 != 0 || c.ldb % 8 != 0 || c.ldc % 8 != 0) return HGEMM_ERR_UNSUPPORTED;
+  if (c.M > kMaxM || c.N > kMaxN || c.K > kMaxK) return HGEMM_ERR_UNSUPPORTED;
+  if (c.lda > (a_mn ? kMaxLdMN : kMaxLdK) || c.ldb > (b_mn ? kMaxLdMN : kMaxLdK) ||
+      c.ldc > kMaxLdC)
+    return HGEMM_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(c.C) & 15) != 0) return HGEMM_ERR_UNSUPPORTED;
+  if (c.K > 0 &&
+      (((reinterpret_cast<uintptr_t>(c.A) | reinterpret_cast<uintptr_t>(c.B)) & 15) != 0))
     return HGEMM_ERR_UNSUPPORTED;
   return HGEMM_OK;
 }
 
-hgemm_status_t run(int layout, int64_t M, int64_t N, int64_t K, int dtype, const void *A,
-                   const void *B, void *C, void *stream, const hgemm_config_t *cfg) {
-  hgemm_status_t st = validate(M, N, K, dtype, A, B, C);
+hgemm_status_t run(const Call &c, void *stream, const hgemm_config_t *cfg) {
+  hgemm_status_t st = validate(c);
   if (st != HGEMM_OK) return st;
   int kidx = -1, group_m = 0, xcd = 1;
   if (cfg != nullptr) {
@@ -136,25 +174,38 @@ hgemm_status_t run(int layout, int64_t M, int64_t N, int64_t K, int dtype, const
     group_m = cfg->group_m;
     if (cfg->xcd_remap >= 0) xcd = cfg->xcd_remap;
   }
-  if (kidx >= 0 && (kTable[kidx].layout != layout || kTable[kidx].dtype != dtype))
+  if (kidx >= 0 && (kTable[kidx].layout != c.layout || kTable[kidx].dtype != c.dtype))
     return HGEMM_ERR_INVALID_ARG;
-  if (M == 0 || N == 0) return HGEMM_OK;
-  if (kidx < 0) kidx = auto_kernel(layout, dtype, M, N);
+  if (c.M == 0 || c.N == 0) return HGEMM_OK;
+  if (kidx < 0) kidx = auto_kernel(c.layout, c.dtype, c.M, c.N);
   if (kidx < 0) return HGEMM_ERR_UNSUPPORTED;
   const KernelEntry &e = kTable[kidx];
+  if (!e.general) {
+    const bool packed = c.lda == c.K && c.ldb == (b_mn_major(c.layout) ? c.N : c.K) &&
+                        c.ldc == c.N;
+    if (!packed || c.alpha != 1.0f || c.beta != 0.0f) return HGEMM_ERR_UNSUPPORTED;
+  }
   if (group_m == 0) group_m = e.default_group_m;
 
-  const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+  const int64_t tiles = ((c.M + e.bm - 1) / e.bm) * ((c.N + e.bn - 1) / e.bn);
   if (tiles > INT32_MAX) return HGEMM_ERR_UNSUPPORTED;
   GemmArgs a;
-  a.A = static_cast<const uint16_t *>(A);
-  a.B = static_cast<const uint16_t *>(B);
-  a.C = static_cast<uint16_t *>(C);
-  a.M = (int)M;
-  a.N = (int)N;
-  a.K = (int)K;
+  a.A = static_cast<const uint16_t *>(c.A);
+  a.B = static_cast<const uint16_t *>(c.B);
+  a.C = static_cast<uint16_t *>(c.C);
+  a.M = (int)c.M;
+  a.N = (int)c.N;
+  a.K = (int)c.K;
+  a.lda = (int)c.lda;
+  a.ldb = (int)c.ldb;
+  a.ldc = (int)c.ldc;
+  a.alpha = c.alpha;
+  a.beta = c.beta;
   a.group_m = group_m;
   a.xcd_remap = xcd;
+  // hipGetLastError() reports the last error of any earlier runtime call on
+  // this thread too: clear it so that only the launch's own result is seen
+  (void)hipGetLastError();
   hipLaunchKernelGGL(e.fn, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) {
@@ -164,28 +215,58 @@ hgemm_status_t run(int layout, int64_t M, int64_t N, int64_t K, int dtype, const
   return HGEMM_OK;
 }
 
+// The pages' two layouts: packed storage, alpha 1, beta 0.
+Call packed(int layout, int64_t M, int64_t N, int64_t K, int dtype, const void *A, const void *B,
+            void *C) {
+  return Call{layout, M, N, K, dtype, 1.0f, 0.0f, A, B, C,
+              K, layout == kNN ? N : K, N};
+}
+
+// op flags -> layout; -1 if invalid
+int layout_of(int opA, int opB) {
+  if ((opA != HGEMM_OP_N && opA != HGEMM_OP_T) || (opB != HGEMM_OP_N && opB != HGEMM_OP_T))
+    return -1;
+  return (opA == HGEMM_OP_T ? 2 : 0) | (opB == HGEMM_OP_N ? 1 : 0);
+}
+
 }  // namespace
 
 extern "C" {
 
 hgemm_status_t hgemm_tn(int64_t M, int64_t N, int64_t K, int dtype, const void *A,
                         const void *Bt, void *C, void *stream) {
-  return run(kTN, M, N, K, dtype, A, Bt, C, stream, nullptr);
+  return run(packed(kTN, M, N, K, dtype, A, Bt, C), stream, nullptr);
 }
 
 hgemm_status_t hgemm_nn(int64_t M, int64_t N, int64_t K, int dtype, const void *A,
                         const void *B, void *C, void *stream) {
-  return run(kNN, M, N, K, dtype, A, B, C, stream, nullptr);
+  return run(packed(kNN, M, N, K, dtype, A, B, C), stream, nullptr);
 }
 
 hgemm_status_t hgemm_tn_ex(int64_t M, int64_t N, int64_t K, int dtype, const void *A,
                            const void *Bt, void *C, void *stream, const hgemm_config_t *cfg) {
-  return run(kTN, M, N, K, dtype, A, Bt, C, stream, cfg);
+  return run(packed(kTN, M, N, K, dtype, A, Bt, C), stream, cfg);
 }
 
 hgemm_status_t hgemm_nn_ex(int64_t M, int64_t N, int64_t K, int dtype, const void *A,
                            const void *B, void *C, void *stream, const hgemm_config_t *cfg) {
-  return run(kNN, M, N, K, dtype, A, B, C, stream, cfg);
+  return run(packed(kNN, M, N, K, dtype, A, B, C), stream, cfg);
+}
+
+hgemm_status_t hgemm_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
+                             float alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
+                             float beta, void *C, int64_t ldc, void *stream,
+                             const hgemm_config_t *cfg) {
+  const int layout = layout_of(opA, opB);
+  if (layout < 0) return HGEMM_ERR_INVALID_ARG;
+  return run(Call{layout, M, N, K, dtype, alpha, beta, A, B, C, lda, ldb, ldc}, stream, cfg);
+}
+
+hgemm_status_t hgemm_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
+                          float alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
+                          float beta, void *C, int64_t ldc, void *stream) {
+  return hgemm_gemm_ex(opA, opB, M, N, K, dtype, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                       nullptr);
 }
 
 const char *hgemm_status_string(int status) {
@@ -200,7 +281,7 @@ const char *hgemm_status_string(int status) {
 
 int hgemm_last_hip_error(void) { return g_last_hip_error; }
 
-const char *hgemm_version(void) { return "hgemm-gfx950 1.0"; }
+const char *hgemm_version(void) { return "hgemm-gfx950 1.1"; }
 
 int hgemm_kernel_count(void) { return kTableSize; }
 
@@ -217,7 +298,7 @@ const char *hgemm_kernel_info(int index, int *layout, int *dtype, int *bm, int *
 
 int hgemm_auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K) {
   (void)K;
-  if ((layout != kTN && layout != kNN) || (dtype != HGEMM_F16 && dtype != HGEMM_BF16) || M <= 0 ||
+  if (layout < kTN || layout > kAtNN || (dtype != HGEMM_F16 && dtype != HGEMM_BF16) || M <= 0 ||
       N <= 0)
     return -1;
   return auto_kernel(layout, dtype, M, N);

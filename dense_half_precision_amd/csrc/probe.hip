@@ -149,6 +149,10 @@ void lds_offsets(int rows, int *offsets) {
     for (int c = 0; c < 8; ++c) offsets[r * 8 + c] = r * T::ROWB + chunk_pos<LDS>(r, c) * 16;
 }
 
+// hipGetLastError() also reports earlier runtime calls on this thread: each
+// launching probe clears it first (clear_error), then checks its own launch.
+void clear_error() { (void)hipGetLastError(); }
+
 hgemm_status_t launched() {
   return hipGetLastError() == hipSuccess ? HGEMM_OK : HGEMM_ERR_HIP;
 }
@@ -158,6 +162,7 @@ hgemm_status_t launched() {
 extern "C" {
 
 hgemm_status_t hgemm_probe_mfma(int dtype, const void *x, const void *y, float *d, void *stream) {
+  clear_error();
   if (dtype != HGEMM_F16 && dtype != HGEMM_BF16) return HGEMM_ERR_INVALID_ARG;
   if (!x || !y || !d) return HGEMM_ERR_INVALID_ARG;
   if (((uintptr_t)x | (uintptr_t)y | (uintptr_t)d) & 15) return HGEMM_ERR_UNSUPPORTED;
@@ -172,6 +177,7 @@ hgemm_status_t hgemm_probe_mfma(int dtype, const void *x, const void *y, float *
 
 hgemm_status_t hgemm_probe_lds_roundtrip(int lds_layout, const void *src, void *dst,
                                          void *stream) {
+  clear_error();
   if (!src || !dst) return HGEMM_ERR_INVALID_ARG;
   if (((uintptr_t)src | (uintptr_t)dst) & 15) return HGEMM_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
@@ -200,6 +206,7 @@ hgemm_status_t hgemm_probe_lds_roundtrip(int lds_layout, const void *src, void *
 
 hgemm_status_t hgemm_probe_mfma_peak(int waves, int iters, float *out, uint64_t *clocks,
                                      void *stream) {
+  clear_error();
   if (waves <= 0 || waves % 4 != 0 || iters <= 0 || !out) return HGEMM_ERR_INVALID_ARG;
   hipLaunchKernelGGL(probe_mfma_peak_kernel, dim3(waves / 4), dim3(256), 0, (hipStream_t)stream,
                      iters, out, clocks);
@@ -208,6 +215,7 @@ hgemm_status_t hgemm_probe_mfma_peak(int waves, int iters, float *out, uint64_t 
 
 hgemm_status_t hgemm_probe_lds_read(int workgroups, int iters, int pattern, float *out,
                                     void *stream) {
+  clear_error();
   if (workgroups <= 0 || iters <= 0 || !out) return HGEMM_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   switch (pattern) {
@@ -223,6 +231,7 @@ hgemm_status_t hgemm_probe_lds_read(int workgroups, int iters, int pattern, floa
 hgemm_status_t hgemm_probe_l2_read(int workgroups, int iters, int mode, const void *buf,
                                    uint32_t window_bytes, uint32_t row_stride, float *out,
                                    void *stream) {
+  clear_error();
   if (workgroups <= 0 || iters <= 0 || !buf || !out) return HGEMM_ERR_INVALID_ARG;
   if (row_stride < 128u || (row_stride & 15u)) return HGEMM_ERR_INVALID_ARG;
   if (window_bytes < 65536u || window_bytes > (1u << 30) || (window_bytes & (window_bytes - 1)))

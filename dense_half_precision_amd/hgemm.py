@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(PKG, "libhgemm.so")
 HEADERS = [os.path.join(ROOT, "include", h) for h in ("hgemm.h", "hgemm_probe.h")]
 
 F16, BF16 = 0, 1
-TN, NN = 0, 1
+TN, NN, AT_TN, AT_NN = 0, 1, 2, 3  # kernel layouts (hgemm_kernel_info)
+OP_N, OP_T = 0, 1                  # operation flags of hgemm_gemm
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 DTYPE_CODES = {"f16": F16, "fp16": F16, "float16": F16, "bf16": BF16, "bfloat16": BF16}
 LDS_XOR, LDS_PLAIN, LDS_PAD, LDS_XOR_ROW = 0, 1, 2, 3
@@ -45,6 +46,14 @@ def _lib() -> ctypes.CDLL:
         return _LIB
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    # PyTorch ships its own copy of the HIP runtime under the same soname.  Load
+    # it first, so that this library binds to the runtime that owns torch's
+    # device memory and streams; loaded the other way round the process ends
+    # up with two runtimes and the second one finds no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     gemm = [i64, i64, i64, i32, vp, vp, vp, vp]
@@ -54,6 +63,12 @@ def _lib() -> ctypes.CDLL:
     for name in ("hgemm_tn_ex", "hgemm_nn_ex"):
         getattr(lib, name).argtypes = gemm + [ctypes.POINTER(Config)]
         getattr(lib, name).restype = i32
+    f32 = ctypes.c_float
+    general = [i32, i32, i64, i64, i64, i32, f32, vp, i64, vp, i64, f32, vp, i64, vp]
+    lib.hgemm_gemm.argtypes = general
+    lib.hgemm_gemm.restype = i32
+    lib.hgemm_gemm_ex.argtypes = general + [ctypes.POINTER(Config)]
+    lib.hgemm_gemm_ex.restype = i32
     lib.hgemm_status_string.argtypes = [i32]
     lib.hgemm_status_string.restype = ctypes.c_char_p
     lib.hgemm_last_hip_error.restype = i32
@@ -123,6 +138,17 @@ def hgemm_tn_ex(M, N, K, dtype, A, Bt, C, stream=0, kernel=-1, group_m=0, xcd_re
 def hgemm_nn_ex(M, N, K, dtype, A, B, C, stream=0, kernel=-1, group_m=0, xcd_remap=-1) -> int:
     cfg = Config(kernel, group_m, xcd_remap, 0)
     return _lib().hgemm_nn_ex(M, N, K, _dt(dtype), A, B, C, stream, ctypes.byref(cfg))
+
+
+def hgemm_gemm(opA, opB, M, N, K, dtype, alpha, A, lda, B, ldb, beta, C, ldc, stream=0,
+               kernel=None, group_m=0, xcd_remap=-1) -> int:
+    """General form (see include/hgemm.h); with `kernel` set, hgemm_gemm_ex."""
+    args = (opA, opB, M, N, K, _dt(dtype), float(alpha), A, lda, B, ldb, float(beta), C, ldc,
+            stream)
+    if kernel is None and group_m == 0 and xcd_remap == -1:
+        return _lib().hgemm_gemm(*args)
+    cfg = Config(-1 if kernel is None else kernel, group_m, xcd_remap, 0)
+    return _lib().hgemm_gemm_ex(*args, ctypes.byref(cfg))
 
 
 def kernel_table() -> list[dict]:
@@ -210,6 +236,37 @@ def matmul_nn(A, B, out=None, stream=None, **cfg):
         st = hgemm_nn(M, N, K, dt, A.data_ptr(), B.data_ptr(), out.data_ptr(), sp)
     _check(st, "hgemm_nn")
     return out
+
+
+def gemm(A, B, C=None, alpha=1.0, beta=0.0, transA=False, transB=False, stream=None, **cfg):
+    """C = alpha * op(A) @ op(B) + beta * C for 2-D CUDA tensors of one dtype.
+
+    op(X) is X, or X.T when the trans flag is set (the tensor then holds the
+    operand stored transposed).  Rows may be strided (leading dimension =
+    stride(0)); columns must be contiguous.  With beta == 0, C (if given) is
+    only written.
+    """
+    import torch
+    for name, t in (("A", A), ("B", B)):
+        if t.dim() != 2 or not t.is_cuda or t.stride(1) != 1:
+            raise ValueError(f"{name} must be a 2-D CUDA tensor with contiguous rows")
+    M, K = (A.shape[1], A.shape[0]) if transA else (A.shape[0], A.shape[1])
+    K2, N = (B.shape[1], B.shape[0]) if transB else (B.shape[0], B.shape[1])
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have one dtype")
+    if C is None:
+        if beta != 0:
+            raise ValueError("beta != 0 needs C")
+        C = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    elif C.shape != (M, N) or C.dtype != A.dtype or C.stride(1) != 1:
+        raise ValueError("C must be [M, N] of the input dtype with contiguous rows")
+    st = hgemm_gemm(OP_T if transA else OP_N, OP_T if transB else OP_N, M, N, K,
+                    _torch_dtype_code(A), alpha, A.data_ptr(), A.stride(0), B.data_ptr(),
+                    B.stride(0), beta, C.data_ptr(), C.stride(0), _stream_ptr(stream), **cfg)
+    _check(st, "hgemm_gemm")
+    return C
 
 
 def probe_mfma(dtype, x_ptr, y_ptr, d_ptr, stream=0) -> int:

@@ -76,13 +76,47 @@ hgemm_status_t hgemm_tn(int64_t M, int64_t N, int64_t K, int dtype,
 hgemm_status_t hgemm_nn(int64_t M, int64_t N, int64_t K, int dtype,
                         const void *A, const void *B, void *C, void *stream);
 
+/*
+ * General form (the BLAS gemm update on row-major storage):
+ *
+ *     C[m][n] = round( alpha * sum_k opA(A)[m][k] * opB(B)[k][n] + beta * C[m][n] )
+ *
+ *   opA = HGEMM_OP_N: A is M x K, element (m, k) at A[m*lda + k], lda >= K;
+ *   opA = HGEMM_OP_T: A is stored K x M, element (m, k) at A[k*lda + m], lda >= M;
+ *   opB = HGEMM_OP_N: B is K x N, element (k, n) at B[k*ldb + n], ldb >= N;
+ *   opB = HGEMM_OP_T: B is stored N x K, element (k, n) at B[n*ldb + k], ldb >= K;
+ *   C is M x N, element (m, n) at C[m*ldc + n], ldc >= N.
+ *
+ * hgemm_tn is (OP_N, OP_T) and hgemm_nn is (OP_N, OP_N), with packed leading
+ * dimensions, alpha = 1 and beta = 0.  The pages stop at C = A*B; alpha and
+ * beta follow the usual BLAS gemm meaning: the FP32 sum is scaled by alpha,
+ * beta times the old C (converted exactly to FP32) is added with one fused
+ * multiply-add, and the result is rounded once to the output type.  With
+ * beta == 0 the old C is not read (it may hold anything, NaN included); with
+ * K == 0 the call computes beta * C.  Leading dimensions are in elements.
+ *
+ * Accepted arguments, beyond those of hgemm_tn: leading dimensions at least
+ * the minimums above (else HGEMM_ERR_INVALID_ARG) and multiples of 8; M a
+ * multiple of 8 when opA is HGEMM_OP_T; lda/ldb at most 2^22 for a K-contiguous
+ * operand (OP_N A, OP_T B) and 2^23 for an M/N-contiguous one, ldc below 2^31
+ * (else HGEMM_ERR_UNSUPPORTED).  With beta != 0, C must not overlap A or B.
+ */
+typedef enum hgemm_op {
+  HGEMM_OP_N = 0, /* operand used as stored */
+  HGEMM_OP_T = 1  /* operand stored transposed */
+} hgemm_op_t;
+
+hgemm_status_t hgemm_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
+                          float alpha, const void *A, int64_t lda, const void *B,
+                          int64_t ldb, float beta, void *C, int64_t ldc, void *stream);
+
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char *hgemm_status_string(int status);
 
 /* hipError_t of this thread's last HGEMM_ERR_HIP (0 if none yet). */
 int hgemm_last_hip_error(void);
 
-/* Library version string, e.g. "hgemm-gfx950 1.0". */
+/* Library version string, e.g. "hgemm-gfx950 1.1". */
 const char *hgemm_version(void);
 
 /*
@@ -110,23 +144,31 @@ hgemm_status_t hgemm_tn_ex(int64_t M, int64_t N, int64_t K, int dtype,
 hgemm_status_t hgemm_nn_ex(int64_t M, int64_t N, int64_t K, int dtype,
                            const void *A, const void *B, void *C, void *stream,
                            const hgemm_config_t *cfg);
+/* As hgemm_gemm, with an explicit configuration (NULL = automatic). */
+hgemm_status_t hgemm_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K,
+                             int dtype, float alpha, const void *A, int64_t lda,
+                             const void *B, int64_t ldb, float beta, void *C,
+                             int64_t ldc, void *stream, const hgemm_config_t *cfg);
 
 /* Number of entries in the kernel table. */
 int hgemm_kernel_count(void);
 
 /* Description of kernel table entry `index` (NULL if out of range):
- * "<layout>_<dtype>_<BM>x<BN>x<BK>" for the production kernels (entries
- * 0..11, the ones the automatic choice uses), with a suffix naming what an
+ * "<layout>_<dtype>_<BM>x<BN>x<BK>" for the production kernels (the ones the
+ * automatic choice uses: entries 0..11 and 20..31; "at_" layouts take A
+ * stored transposed), with a suffix naming what an
  * ablation changes ("_plainlds": LDS without the XOR swizzle, "_directepi":
  * epilogue without LDS staging), and an "rs_" prefix for the register-staged
  * 32x32x16 baseline design (suffix: its LDS layout).  The integers describing
- * it are written through the non-NULL pointers: layout 0 = TN, 1 = NN; dtype
+ * it are written through the non-NULL pointers: layout 0 = TN (A[M][K],
+ * Bt[N][K]), 1 = NN (A[M][K], B[K][N]), 2 = at_tn (At[K][M], Bt[N][K]), 3 =
+ * at_nn (At[K][M], B[K][N]); dtype
  * as hgemm_dtype_t; the workgroup tile BM x BN x BK. */
 const char *hgemm_kernel_info(int index, int *layout, int *dtype, int *bm,
                               int *bn, int *bk);
 
 /* Kernel table index the automatic choice would use for this call (layout
- * 0 = TN, 1 = NN), or -1 for invalid arguments.  The choice takes the tile
+ * as in hgemm_kernel_info), or -1 for invalid arguments.  The choice takes the tile
  * size (256, 128 or 64, square) with the least estimated time: waves of
  * workgroups over the 256 CUs times one tile's area over that tile size's
  * relative throughput (1, 0.8, 0.5); ties go to the larger tile. */

@@ -109,5 +109,34 @@ def gpu_gemm(layout: str, dtype: str, A_bits: np.ndarray, B_bits: np.ndarray, ke
     fn = hgemm.hgemm_tn_ex if layout == "tn" else hgemm.hgemm_nn_ex
     st = fn(M, N, K, dtype, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), stream_ptr(),
             kernel=kernel, group_m=group_m, xcd_remap=xcd_remap)
-    assert st == hgemm.OK, f"{layout} {dtype} {M}x{N}x{K}: status {st}"
+    assert st == hgemm.OK, (f"{layout} {dtype} {M}x{N}x{K}: status {st}, hipError_t "
+                            f"{hgemm.lib().hgemm_last_hip_error()}")
+    return to_host(dC)
+
+
+def stored(logical: np.ndarray, transposed: bool, pad: int, fill: int = 0) -> np.ndarray:
+    """A logical matrix (or its transpose) in a buffer whose rows are `pad`
+    elements longer than needed; the row length is the leading dimension."""
+    src = logical.T if transposed else logical
+    out = np.full((src.shape[0], src.shape[1] + pad), fill, dtype=np.uint16)
+    out[:, :src.shape[1]] = src
+    return out
+
+
+def gpu_gemm_general(opA: int, opB: int, dtype: str, M: int, N: int, K: int, A_st: np.ndarray,
+                     B_st: np.ndarray, alpha: float = 1.0, beta: float = 0.0,
+                     C_st: np.ndarray | None = None, kernel: int | None = None) -> np.ndarray:
+    """hgemm_gemm through the C ABI on stored operands (leading dimension =
+    stored row length); returns the whole stored C.  Without C_st, C is an
+    M x (N + 8) buffer of NaN patterns, so that both unwritten elements and
+    writes into the padding show."""
+    from dense_half_precision_amd import hgemm
+    if C_st is None:
+        C_st = np.full((M, N + 8), 0x7E00 if dtype == "f16" else 0x7FC0, dtype=np.uint16)
+    dA, dB, dC = to_dev(A_st), to_dev(B_st), to_dev(C_st)
+    st = hgemm.hgemm_gemm(opA, opB, M, N, K, dtype, alpha, dA.data_ptr(), A_st.shape[1],
+                          dB.data_ptr(), B_st.shape[1], beta, dC.data_ptr(), C_st.shape[1],
+                          stream_ptr(), kernel=kernel)
+    assert st == hgemm.OK, (f"gemm op{opA}{opB} {dtype} {M}x{N}x{K}: status {st}, hipError_t "
+                            f"{hgemm.lib().hgemm_last_hip_error()}")
     return to_host(dC)

@@ -36,7 +36,8 @@ def _regs(text: str) -> frozenset:
 
 def kernel_bodies(asm: str, prefix: str) -> dict:
     """Map each function whose symbol starts with ``prefix`` to its lines
-    (label to s_endpgm)."""
+    (from its label to its .Lfunc_end label; a kernel may end in several
+    s_endpgm)."""
     out, cur, name = {}, None, None
     for line in asm.splitlines():
         if cur is None:
@@ -44,10 +45,11 @@ def kernel_bodies(asm: str, prefix: str) -> dict:
             if m and m.group(1).startswith(prefix):
                 name, cur = m.group(1), []
             continue
-        cur.append(line)
-        if line.strip().startswith("s_endpgm"):
+        if line.startswith(".Lfunc_end"):
             out[name] = cur
             cur = None
+            continue
+        cur.append(line)
     return out
 
 

@@ -54,6 +54,39 @@ def test_validation_codes(fn):
     assert fn(8, 0, 8, 1, 0, 0, 0) == hgemm.OK
 
 
+def test_general_validation_codes():
+    """hgemm_gemm: operation flags, leading dimensions, limits (nothing launches)."""
+    g = hgemm.hgemm_gemm
+    inv, uns, ok = hgemm.ERR_INVALID_ARG, hgemm.ERR_UNSUPPORTED, hgemm.OK
+    N_, T_ = hgemm.OP_N, hgemm.OP_T
+    M, N, K = 16, 24, 32
+    # minimum leading dimensions per flag
+    assert g(N_, N_, M, N, K, 0, 1, FAKE, K - 8, FAKE, N, 0, FAKE, N) == inv   # lda < K
+    assert g(T_, N_, M, N, K, 0, 1, FAKE, M - 8, FAKE, N, 0, FAKE, N) == inv   # lda < M
+    assert g(N_, N_, M, N, K, 0, 1, FAKE, K, FAKE, N - 8, 0, FAKE, N) == inv   # ldb < N
+    assert g(N_, T_, M, N, K, 0, 1, FAKE, K, FAKE, K - 8, 0, FAKE, N) == inv   # ldb < K
+    assert g(N_, N_, M, N, K, 0, 1, FAKE, K, FAKE, N, 0, FAKE, N - 8) == inv   # ldc < N
+    assert g(2, N_, M, N, K, 0, 1, FAKE, K, FAKE, N, 0, FAKE, N) == inv        # bad flag
+    assert g(N_, -1, M, N, K, 0, 1, FAKE, K, FAKE, N, 0, FAKE, N) == inv
+    # multiples of 8 and limits
+    assert g(N_, N_, M, N, K, 0, 1, FAKE, K + 4, FAKE, N, 0, FAKE, N) == uns   # lda % 8
+    assert g(N_, N_, M, N, K, 0, 1, FAKE, K, FAKE, N, 0, FAKE, N + 4) == uns   # ldc % 8
+    assert g(T_, N_, 12, N, K, 0, 1, FAKE, 16, FAKE, N, 0, FAKE, N) == uns     # M % 8, A^T
+    assert g(N_, T_, M, N, K, 0, 1, FAKE, (1 << 22) + 8, FAKE, K, 0, FAKE, N) == uns
+    assert g(T_, N_, M, N, K, 0, 1, FAKE, (1 << 23) + 8, FAKE, N, 0, FAKE, N) == uns
+    assert g(N_, N_, M, N, K, 0, 1, FAKE, K, FAKE, (1 << 23) + 8, 0, FAKE, N) == uns
+    assert g(N_, N_, M, N, K, 0, 1, FAKE, K, FAKE, N, 0, FAKE + 8, N) == uns   # misaligned C
+    # empty output: a no-op even with NULL pointers
+    assert g(T_, T_, 0, N, K, 0, 1, 0, K, 0, K, 0, 0, N) == ok
+    # the register-staged baseline only takes packed operands, alpha 1, beta 0
+    rs = hgemm.kernel_index("rs_tn_f16_256x256x64_xor")
+    assert g(N_, T_, M, N, K, 0, 1, FAKE, K + 8, FAKE, K, 0, FAKE, N, kernel=rs) == uns
+    assert g(N_, T_, M, N, K, 0, 2.0, FAKE, K, FAKE, K, 0, FAKE, N, kernel=rs) == uns
+    # a kernel of another layout
+    nn = hgemm.kernel_index("nn_f16_256x256x64")
+    assert g(N_, T_, M, N, K, 0, 1, FAKE, K, FAKE, K, 0, FAKE, N, kernel=nn) == inv
+
+
 def test_ex_config_validation():
     inv = hgemm.ERR_INVALID_ARG
     tab = hgemm.kernel_table()
@@ -74,18 +107,18 @@ def test_kernel_table_and_auto_choice():
     assert len(tab) == hgemm.lib().hgemm_kernel_count() > 0
     assert hgemm.lib().hgemm_kernel_info(len(tab), None, None, None, None, None) is None
     for k in tab:
-        assert k["layout"] in (0, 1) and k["dtype"] in (0, 1) and k["bk"] == 64
-        lay = "tn" if k["layout"] == 0 else "nn"
+        assert k["layout"] in (0, 1, 2, 3) and k["dtype"] in (0, 1) and k["bk"] == 64
+        lay = ("tn", "nn", "at_tn", "at_nn")[k["layout"]]
         stem = k["name"][3:] if k["name"].startswith("rs_") else k["name"]
         assert stem.startswith(f"{lay}_{'f16' if k['dtype'] == 0 else 'bf16'}_")
     # every layout/dtype has an automatic choice, matching layout and dtype
-    for lay in (0, 1):
+    for lay in (0, 1, 2, 3):
         for dt in (0, 1):
             for M, N in ((1, 8), (512, 512), (2048, 2048), (8192, 8192)):
                 i = hgemm.auto_kernel(lay, dt, M, N, 64)
                 assert 0 <= i < len(tab)
                 assert tab[i]["layout"] == lay and tab[i]["dtype"] == dt
-    assert hgemm.auto_kernel(2, 0, 8, 8, 8) == -1
+    assert hgemm.auto_kernel(4, 0, 8, 8, 8) == -1
     assert hgemm.auto_kernel(0, 0, 0, 8, 8) == -1
     # the large configurations get the 256 x 256 tile, the square 2048 the 128 one
     assert tab[hgemm.auto_kernel(0, 0, 8192, 8192, 8192)]["bm"] == 256

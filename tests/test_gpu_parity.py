@@ -57,12 +57,13 @@ def test_edge_shapes_auto(layout, dtype):
         helpers.parity(C, oracle.hgemm(layout, dtype, A, B), dtype, f"{layout} {dtype} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("kernel", range(24))
+@pytest.mark.parametrize("kernel", range(20))
 def test_every_kernel_ragged(kernel):
+    """The TN/NN entries of the table (the transposed-A ones are covered by
+    the general-form tests)."""
     tab = hgemm.kernel_table()
-    if kernel >= len(tab):
-        pytest.skip("no such kernel")
     k = tab[kernel]
+    assert k["layout"] in (hgemm.TN, hgemm.NN)
     layout = "tn" if k["layout"] == hgemm.TN else "nn"
     dtype = "f16" if k["dtype"] == hgemm.F16 else "bf16"
     w = inputs.Workload(0, layout, dtype, 0, 0, 0, "normal")
