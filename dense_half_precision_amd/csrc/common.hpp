@@ -83,6 +83,60 @@ __host__ __device__ __forceinline__ int nn_chunk_xor(int k, int row_bytes) {
   }
 }
 
+// ---- operand tiles: direct-to-LDS placement and fragment reads ------------
+// One K step of an operand tile in LDS, as the kernels load and read it.
+//
+// K-contiguous operand (A[M][K], Bt[N][K]): rows of 64 k = 128 bytes, chunk c
+// of row r at chunk_pos(r, c).  Load segment `seg` (1 KiB, one wave
+// instruction) covers rows 8*seg .. 8*seg+7; lane l writes LDS bytes
+// seg*1024 + 16*l, i.e. row 8*seg + l/8, physical chunk l%8, and so loads the
+// logical chunk (l%8) ^ chunk_pos(row, 0) (the XOR layouts are involutions).
+// Returns the global byte offset of that chunk (row stride `ld` elements);
+// the logical chunk goes to `chunk`.
+template <int LDS>
+__host__ __device__ __forceinline__ uint32_t kmajor_load_offset(int seg, int lane, int ld,
+                                                                int &chunk) {
+  const int row = seg * 8 + (lane >> 3);
+  chunk = (lane & 7) ^ chunk_pos<LDS>(row, 0);
+  return (uint32_t)(row * ld + chunk * 8) * 2u;
+}
+
+// M/N-contiguous operand (At[K][M], B[K][N]): k-rows of `rowb` (2 * tile
+// width) bytes; a segment holds 1024 / rowb k-rows; lane l writes k-row
+// seg*rps + l/cpr, physical chunk l%cpr, which holds logical chunk
+// (l%cpr) ^ nn_chunk_xor(k).  Chunks at or past `xdim` (the M or N edge, a
+// multiple of 8) relative to the tile origin x0 get an out-of-range offset.
+template <int LDS>
+__host__ __device__ __forceinline__ uint32_t mnmajor_load_offset(int seg, int lane, int ld,
+                                                                 int rowb, int x0, int xdim,
+                                                                 int &chunk) {
+  const int cpr = rowb / 16, rps = 1024 / rowb;
+  const int k = seg * rps + lane / cpr;
+  const int c = (lane % cpr) ^ nn_chunk_xor<LDS>(k, rowb);
+  chunk = c;
+  return (x0 + c * 8 < xdim) ? (uint32_t)(k * ld + c * 8) * 2u : kOutOfRange;
+}
+
+// Matrix-core operand fragment: lane l holds 8 consecutive k (k = 32*sl +
+// 8*(l/16) + e, e = 0..7) of row/column 16*f + l%16 of the tile.
+// K-contiguous: one 16-byte read at f*16*128 + kmajor_frag_offset(l, sl).
+template <int LDS>
+__host__ __device__ __forceinline__ uint32_t kmajor_frag_offset(int lane, int sl) {
+  return (lane & 15) * 128 + chunk_pos<LDS>(lane & 15, 4 * sl + (lane >> 4)) * 16;
+}
+
+// M/N-contiguous: two transposing reads (ds_read_b64_tr_b16) at
+// mnmajor_frag_offset(l, x, rowb) + (32*sl + 4*h) * rowb, h = 0, 1, for the
+// fragment at columns x .. x+15 (x a multiple of 16): within each 16-lane
+// group, lane i points at k-row 8g + i/4 (+4h), columns x + 4*(i%4) .. +3.
+template <int LDS>
+__host__ __device__ __forceinline__ uint32_t mnmajor_frag_offset(int lane, int x, int rowb) {
+  const int g = lane >> 4, i = lane & 15;
+  const int k = 8 * g + (i >> 2);
+  const int c = ((x / 8) ^ nn_chunk_xor<LDS>(k, rowb)) + ((i & 3) >> 1);
+  return k * rowb + c * 16 + (i & 1) * 8;
+}
+
 // Map the dispatch index to (tile_m, tile_n).
 __host__ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n,
                                                      int group_m, int xcd_remap, int &tm,

@@ -126,18 +126,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   // m/n-chunk (lane%CPR) ^ nn_chunk_xor(k); chunks past the M/N edge (a
   // multiple of 8) read out of range.
   // Wave w loads segments w*SEG .. w*SEG+SEG-1 of each operand.
-  const int seg_row = lane >> 3, pchunk = lane & 7;
   auto kmaj_off = [&](int seg, int ld, int &chunk) {
-    const int row = seg * 8 + seg_row;
-    chunk = pchunk ^ (chunk_pos<T::LDS>(row, 0));
-    return (uint32_t)(row * ld + chunk * 8) * 2u;
+    return kmajor_load_offset<T::LDS>(seg, lane, ld, chunk);
   };
   auto mnmaj_off = [&](int seg, int ld, int rowb, int x0, int xdim, int &chunk) {
-    const int cpr = rowb / 16, rps = 1024 / rowb;
-    const int k = seg * rps + lane / cpr;
-    const int c = (lane % cpr) ^ nn_chunk_xor<T::LDS>(k, rowb);
-    chunk = c;
-    return (x0 + c * 8 < xdim) ? (uint32_t)(k * ld + c * 8) * 2u : kOutOfRange;
+    return mnmajor_load_offset<T::LDS>(seg, lane, ld, rowb, x0, xdim, chunk);
   };
   uint32_t a_off[SEG_A];
   int a_chunk[SEG_A];
@@ -203,22 +196,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   // 4*slice + lane/16 of that row.
   uint32_t rd_off[2];
 #pragma unroll
-  for (int sl = 0; sl < 2; ++sl)
-    rd_off[sl] = (lane & 15) * 128 + chunk_pos<T::LDS>(lane & 15, 4 * sl + (lane >> 4)) * 16;
+  for (int sl = 0; sl < 2; ++sl) rd_off[sl] = kmajor_frag_offset<T::LDS>(lane, sl);
   const uint32_t rd_a = (wm * T::WTM) * 128;
   const uint32_t rd_b = (wn * T::WTN) * 128;
-  // m/n-contiguous: lane i of group g points at k-row 8g + i/4 (+4 for the
-  // second read) of slice sl, m/n = 16j + 4*(i%4) .. +3 of the wave's block.
+  // m/n-contiguous: two transposing reads per fragment (see mnmajor_frag_offset)
   auto tr_offsets = [&](uint32_t *off, int nfrag, int x_wave, int rowb) {
-    const int g = lane >> 4, i = lane & 15;
-    const int k = 8 * g + (i >> 2);
-    const int fx = nn_chunk_xor<T::LDS>(k, rowb);
 #pragma unroll
-    for (int j = 0; j < nfrag; ++j) {
-      const int cbase = (x_wave + 16 * j) / 8;  // even chunk index
-      const int c = (cbase ^ fx) + ((i & 3) >> 1);
-      off[j] = k * rowb + c * 16 + (i & 1) * 8;
-    }
+    for (int j = 0; j < nfrag; ++j) off[j] = mnmajor_frag_offset<T::LDS>(lane, x_wave + 16 * j, rowb);
   };
   uint32_t tra_off[A_MN ? FM : 1], trb_off[B_MN ? FN : 1];
   if constexpr (A_MN) tr_offsets(tra_off, FM, wm * T::WTM, 2 * BM);

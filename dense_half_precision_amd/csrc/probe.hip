@@ -20,7 +20,61 @@ __global__ __launch_bounds__(64) void probe_mfma_kernel(const u32x4 *x, const u3
   for (int r = 0; r < 16; ++r) d[l * 16 + r] = acc[r];
 }
 
-// Same store/read pattern as gemm_kernel's A region with BM = 256, 256 threads.
+// One 16x16x32 matrix-core instruction on one wave.
+template <int DT>
+__global__ __launch_bounds__(64) void probe_mfma16_kernel(const u32x4 *x, const u32x4 *y,
+                                                          float *d) {
+  const int l = threadIdx.x;
+  const f32x4 acc = mfma16x16x32<DT>(x[l], y[l], f32x4{});
+#pragma unroll
+  for (int r = 0; r < 4; ++r) d[l * 4 + r] = acc[r];
+}
+
+// One wave loads one K step of an operand tile (BX rows x 64 k, or 64 k-rows
+// x BX for the m/n-contiguous form) into LDS with the kernels' direct-to-LDS
+// placement and XOR layout, then reads every operand fragment back with the
+// kernels' fragment reads: dst[f][sl][lane] = the 16 bytes lane `lane` holds
+// for fragment f (rows/columns 16f..16f+15) of k-slice sl.
+template <int MN, int BX>
+__global__ __launch_bounds__(64) void probe_fragments_kernel(const uint16_t *src, int ld,
+                                                             u32x4 *dst) {
+  __shared__ __attribute__((aligned(1024))) char smem[BX * 128];
+  const int lane = threadIdx.x;
+  constexpr int ROWB = 2 * BX;
+  const uint32_t bytes = (uint32_t)((MN ? 63 * ld + BX : (BX - 1) * ld + 64) * 2);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, bytes);
+#pragma unroll
+  for (int seg = 0; seg < BX / 8; ++seg) {  // BX * 128 bytes = BX / 8 segments of 1 KiB
+    int chunk;
+    const uint32_t off = MN ? mnmajor_load_offset<kLdsXor>(seg, lane, ld, ROWB, 0, BX, chunk)
+                            : kmajor_load_offset<kLdsXor>(seg, lane, ld, chunk);
+    load16_lds(r, off, smem + seg * 1024);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));  // the segments have landed in LDS
+#pragma unroll
+  for (int f = 0; f < BX / 16; ++f) {
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      u32x4 v;
+      if constexpr (MN) {
+        const uint32_t a = lds_addr(smem + mnmajor_frag_offset<kLdsXor>(lane, 16 * f, ROWB));
+        const u32x2 lo = lds_read_tr16(a, (32 * sl) * ROWB);
+        const u32x2 hi = lds_read_tr16(a, (32 * sl + 4) * ROWB);
+        v[0] = lo[0];
+        v[1] = lo[1];
+        v[2] = hi[0];
+        v[3] = hi[1];
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v));  // the reads are not compiler-tracked
+      } else {
+        v = *(const u32x4 *)(smem + f * 16 * 128 + kmajor_frag_offset<kLdsXor>(lane, sl));
+      }
+      dst[(f * 2 + sl) * 64 + lane] = v;
+    }
+  }
+}
+
+// Same store/read pattern as the register-staged baseline's A region with
+// BM = 256, 256 threads.
 template <int LDS>
 __global__ __launch_bounds__(256) void probe_lds_kernel(const u32x4 *src, u32x4 *dst) {
   using T = RsCfg<256, 256, 2, 2, LDS>;
@@ -173,6 +227,77 @@ hgemm_status_t hgemm_probe_mfma(int dtype, const void *x, const void *y, float *
     hipLaunchKernelGGL(probe_mfma_kernel<kBF16>, dim3(1), dim3(64), 0, (hipStream_t)stream,
                        (const u32x4 *)x, (const u32x4 *)y, d);
   return launched();
+}
+
+hgemm_status_t hgemm_probe_mfma16(int dtype, const void *x, const void *y, float *d,
+                                  void *stream) {
+  clear_error();
+  if (dtype != HGEMM_F16 && dtype != HGEMM_BF16) return HGEMM_ERR_INVALID_ARG;
+  if (!x || !y || !d) return HGEMM_ERR_INVALID_ARG;
+  if (((uintptr_t)x | (uintptr_t)y | (uintptr_t)d) & 15) return HGEMM_ERR_UNSUPPORTED;
+  if (dtype == HGEMM_F16)
+    hipLaunchKernelGGL(probe_mfma16_kernel<kF16>, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                       (const u32x4 *)x, (const u32x4 *)y, d);
+  else
+    hipLaunchKernelGGL(probe_mfma16_kernel<kBF16>, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                       (const u32x4 *)x, (const u32x4 *)y, d);
+  return launched();
+}
+
+hgemm_status_t hgemm_probe_fragments(int mn_major, int bx, const void *src, int64_t ld,
+                                     void *dst, void *stream) {
+  clear_error();
+  if (!src || !dst || (mn_major != 0 && mn_major != 1)) return HGEMM_ERR_INVALID_ARG;
+  if (bx != 64 && bx != 128 && bx != 256) return HGEMM_ERR_INVALID_ARG;
+  if (ld < (mn_major ? bx : 64) || ld % 8 != 0 || ld > (1 << 20)) return HGEMM_ERR_INVALID_ARG;
+  if (((uintptr_t)src | (uintptr_t)dst) & 15) return HGEMM_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  const uint16_t *p = (const uint16_t *)src;
+  u32x4 *q = (u32x4 *)dst;
+  const int l = (int)ld;
+  if (mn_major) {
+    if (bx == 64) hipLaunchKernelGGL((probe_fragments_kernel<1, 64>), dim3(1), dim3(64), 0, s, p, l, q);
+    if (bx == 128) hipLaunchKernelGGL((probe_fragments_kernel<1, 128>), dim3(1), dim3(64), 0, s, p, l, q);
+    if (bx == 256) hipLaunchKernelGGL((probe_fragments_kernel<1, 256>), dim3(1), dim3(64), 0, s, p, l, q);
+  } else {
+    if (bx == 64) hipLaunchKernelGGL((probe_fragments_kernel<0, 64>), dim3(1), dim3(64), 0, s, p, l, q);
+    if (bx == 128) hipLaunchKernelGGL((probe_fragments_kernel<0, 128>), dim3(1), dim3(64), 0, s, p, l, q);
+    if (bx == 256) hipLaunchKernelGGL((probe_fragments_kernel<0, 256>), dim3(1), dim3(64), 0, s, p, l, q);
+  }
+  return launched();
+}
+
+hgemm_status_t hgemm_probe_operand_offsets(int mn_major, int bx, int *load_row, int *load_chunk,
+                                           int *read_off) {
+  if (!load_row || !load_chunk || !read_off || (mn_major != 0 && mn_major != 1))
+    return HGEMM_ERR_INVALID_ARG;
+  if (bx != 64 && bx != 128 && bx != 256) return HGEMM_ERR_INVALID_ARG;
+  const int rowb = 2 * bx;
+  for (int seg = 0; seg < bx / 8; ++seg)
+    for (int l = 0; l < 64; ++l) {
+      int chunk;
+      if (mn_major) {
+        // k-row of the lane's chunk: the offset is k*ld + chunk*8 elements; with ld = 1 << 16
+        // the k-row is recovered from the offset
+        const uint32_t off = mnmajor_load_offset<kLdsXor>(seg, l, 1 << 16, rowb, 0, bx, chunk);
+        load_row[seg * 64 + l] = (int)((off / 2u) >> 16);
+      } else {
+        const uint32_t off = kmajor_load_offset<kLdsXor>(seg, l, 1 << 16, chunk);
+        load_row[seg * 64 + l] = (int)((off / 2u) >> 16);
+      }
+      load_chunk[seg * 64 + l] = chunk;
+    }
+  const int reads = mn_major ? 2 : 1;
+  for (int f = 0; f < bx / 16; ++f)
+    for (int sl = 0; sl < 2; ++sl)
+      for (int r = 0; r < reads; ++r)
+        for (int l = 0; l < 64; ++l) {
+          const int o = mn_major ? (int)mnmajor_frag_offset<kLdsXor>(l, 16 * f, rowb) +
+                                       (32 * sl + 4 * r) * rowb
+                                 : f * 16 * 128 + (int)kmajor_frag_offset<kLdsXor>(l, sl);
+          read_off[((f * 2 + sl) * reads + r) * 64 + l] = o;
+        }
+  return HGEMM_OK;
 }
 
 hgemm_status_t hgemm_probe_lds_roundtrip(int lds_layout, const void *src, void *dst,

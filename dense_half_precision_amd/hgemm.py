@@ -56,6 +56,7 @@ def _lib() -> ctypes.CDLL:
         pass
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    ip = ctypes.POINTER(ctypes.c_int)
     gemm = [i64, i64, i64, i32, vp, vp, vp, vp]
     for name in ("hgemm_tn", "hgemm_nn"):
         getattr(lib, name).argtypes = gemm
@@ -74,13 +75,18 @@ def _lib() -> ctypes.CDLL:
     lib.hgemm_last_hip_error.restype = i32
     lib.hgemm_version.restype = ctypes.c_char_p
     lib.hgemm_kernel_count.restype = i32
-    ip = ctypes.POINTER(ctypes.c_int)
     lib.hgemm_kernel_info.argtypes = [i32, ip, ip, ip, ip, ip]
     lib.hgemm_kernel_info.restype = ctypes.c_char_p
     lib.hgemm_auto_kernel.argtypes = [i32, i32, i64, i64, i64]
     lib.hgemm_auto_kernel.restype = i32
     lib.hgemm_probe_mfma.argtypes = [i32, vp, vp, vp, vp]
     lib.hgemm_probe_mfma.restype = i32
+    lib.hgemm_probe_mfma16.argtypes = [i32, vp, vp, vp, vp]
+    lib.hgemm_probe_mfma16.restype = i32
+    lib.hgemm_probe_fragments.argtypes = [i32, i32, vp, i64, vp, vp]
+    lib.hgemm_probe_fragments.restype = i32
+    lib.hgemm_probe_operand_offsets.argtypes = [i32, i32, ip, ip, ip]
+    lib.hgemm_probe_operand_offsets.restype = i32
     lib.hgemm_probe_lds_roundtrip.argtypes = [i32, vp, vp, vp]
     lib.hgemm_probe_lds_roundtrip.restype = i32
     lib.hgemm_probe_mfma_peak.argtypes = [i32, i32, vp, vp, vp]
@@ -273,6 +279,14 @@ def probe_mfma(dtype, x_ptr, y_ptr, d_ptr, stream=0) -> int:
     return _lib().hgemm_probe_mfma(_dt(dtype), x_ptr, y_ptr, d_ptr, stream)
 
 
+def probe_mfma16(dtype, x_ptr, y_ptr, d_ptr, stream=0) -> int:
+    return _lib().hgemm_probe_mfma16(_dt(dtype), x_ptr, y_ptr, d_ptr, stream)
+
+
+def probe_fragments(mn_major, bx, src_ptr, ld, dst_ptr, stream=0) -> int:
+    return _lib().hgemm_probe_fragments(mn_major, bx, src_ptr, ld, dst_ptr, stream)
+
+
 def probe_lds_roundtrip(lds_layout, src_ptr, dst_ptr, stream=0) -> int:
     return _lib().hgemm_probe_lds_roundtrip(lds_layout, src_ptr, dst_ptr, stream)
 
@@ -285,6 +299,21 @@ def tile_order(tiles_m, tiles_n, group_m, xcd_remap):
     _check(_lib().hgemm_probe_tile_order(tiles_m, tiles_n, group_m, xcd_remap, tm, tn),
            "hgemm_probe_tile_order")
     return list(tm), list(tn)
+
+
+def operand_offsets(mn_major: int, bx: int):
+    """The production kernels' LDS placement of one operand K step (host-side
+    code): (load_row, load_chunk) per [segment][lane], read_off per
+    [fragment][slice][read][lane]."""
+    import numpy as np
+    reads = 2 if mn_major else 1
+    lr = (ctypes.c_int * (bx // 8 * 64))()
+    lc = (ctypes.c_int * (bx // 8 * 64))()
+    ro = (ctypes.c_int * (bx // 16 * 2 * reads * 64))()
+    _check(_lib().hgemm_probe_operand_offsets(mn_major, bx, lr, lc, ro),
+           "hgemm_probe_operand_offsets")
+    return (np.array(lr).reshape(bx // 8, 64), np.array(lc).reshape(bx // 8, 64),
+            np.array(ro).reshape(bx // 16, 2, reads, 64))
 
 
 def lds_offsets(lds_layout, rows=256):

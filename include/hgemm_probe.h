@@ -31,8 +31,55 @@ hgemm_status_t hgemm_probe_mfma(int dtype, const void *x, const void *y, float *
                                 void *stream);
 
 /*
+ * One 16x16x32 matrix-core instruction on one wave (the shape of the
+ * production kernels).
+ * x, y: 64 lanes x 8 elements of `dtype` (lane-major, 1024 bytes each), the
+ *       first and second operand as each lane holds it.
+ * d:    64 lanes x 4 floats (lane-major, 1024 bytes): the accumulator
+ *       registers after D = X * Y with a zero input accumulator.
+ */
+hgemm_status_t hgemm_probe_mfma16(int dtype, const void *x, const void *y, float *d,
+                                  void *stream);
+
+/*
+ * One K step of an operand tile through the production kernels' path: one
+ * wave loads it into LDS with their direct-to-LDS placement and XOR layout,
+ * then reads every matrix-core operand fragment back with their fragment
+ * reads (16-byte reads for a K-contiguous operand, transposing reads for an
+ * M/N-contiguous one).
+ *   mn_major 0: src holds a bx x 64 tile, element (row, k) at src[row*ld + k]
+ *               (ld >= 64);
+ *   mn_major 1: src holds the same tile stored 64 x bx, element (row, k) at
+ *               src[k*ld + row] (ld >= bx);
+ *   bx in {64, 128, 256}; ld a multiple of 8, at most 2^20.
+ * dst: (bx/16) x 2 x 64 entries of 16 bytes: entry [f][sl][lane] holds the 8
+ *      values lane `lane` feeds the matrix core for fragment f and k-slice sl,
+ *      which must be tile (16f + lane%16, 32sl + 8(lane/16) + e), e = 0..7.
+ * The check of the fragment-to-operand map of the ablation draft's section
+ * 3.1-3.2 for this hardware.
+ */
+hgemm_status_t hgemm_probe_fragments(int mn_major, int bx, const void *src, int64_t ld,
+                                     void *dst, void *stream);
+
+/*
+ * Host-side: the production kernels' placement of one K step of an operand
+ * tile (bx in {64, 128, 256}; XOR layout), computed by the same functions
+ * the kernels use.
+ *   load_row[s*64 + l], load_chunk[s*64 + l] (bx/8 segments x 64 lanes): the
+ *     tile row (mn_major 0) or k-row (mn_major 1) and the logical 16-byte
+ *     chunk that lane l of direct-to-LDS segment s loads; it lands at LDS byte
+ *     s*1024 + 16*l.
+ *   read_off[((f*2 + sl)*R + r)*64 + l] ((bx/16) x 2 x R x 64; R = 1 for
+ *     mn_major 0, 2 for mn_major 1): the LDS byte offset lane l reads with
+ *     read r of fragment f, k-slice sl (16-byte reads, or 8-byte transposing
+ *     reads).
+ */
+hgemm_status_t hgemm_probe_operand_offsets(int mn_major, int bx, int *load_row, int *load_chunk,
+                                           int *read_off);
+
+/*
  * LDS layout round trip for a 256-row x 64-column tile of 16-bit values:
- * the tile is written to LDS with the kernels' store pattern and LDS layout
+ * the tile is written to LDS with the register-staged baseline's store pattern and LDS layout
  * `lds_layout` (0 = XOR swizzle on row/2, 1 = plain rows, 2 = padded rows,
  * 3 = XOR swizzle on the row), read back
  * with the kernels' operand-fragment pattern, and each fragment is stored

@@ -69,3 +69,49 @@ def test_lds_roundtrip(layout):
     assert hgemm.probe_lds_roundtrip(layout, ds.data_ptr(), dd.data_ptr(),
                                      helpers.stream_ptr()) == hgemm.OK
     assert np.array_equal(helpers.to_host(dd), src)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_mfma16_lane_map(dtype):
+    """16x16x32 (the production shape): lane l holds X[l%16][8*(l//16)+e] and
+    Y[8*(l//16)+e][l%16]; accumulator r of lane l is D[4*(l//16) + r][l%16].
+    Small integers keep every product and sum exact."""
+    import torch
+    g = np.random.Generator(np.random.PCG64(5))
+    X = g.integers(-3, 4, size=(16, 32))
+    Y = g.integers(-3, 4, size=(32, 16))
+    D = X @ Y
+    lane = np.arange(64)
+    e = np.arange(8)
+    xl = X[(lane % 16)[:, None], (8 * (lane // 16))[:, None] + e[None, :]]
+    yl = Y[(8 * (lane // 16))[:, None] + e[None, :], (lane % 16)[:, None]]
+    dx, dy = helpers.to_dev(_bits(xl, dtype)), helpers.to_dev(_bits(yl, dtype))
+    dd = torch.full((64, 4), float("nan"), dtype=torch.float32, device="cuda")
+    assert hgemm.probe_mfma16(dtype, dx.data_ptr(), dy.data_ptr(), dd.data_ptr(),
+                              helpers.stream_ptr()) == hgemm.OK
+    r = np.arange(4)
+    want = D[4 * (lane[:, None] // 16) + r[None, :], (lane % 16)[:, None]]
+    assert np.array_equal(dd.cpu().numpy(), want.astype(np.float32))
+
+
+@pytest.mark.parametrize("mn_major", [0, 1])
+@pytest.mark.parametrize("bx", [64, 128, 256])
+def test_operand_fragments(mn_major, bx):
+    """One K step through the production path (direct-to-LDS placement, XOR
+    layout, 16-byte or transposing fragment reads) delivers exactly the
+    matrix-core operand: lane l of fragment f, slice sl holds tile element
+    (16f + l%16, 32sl + 8(l//16) + e).  Random bit patterns, padded rows."""
+    import torch
+    tile = np.random.Generator(np.random.PCG64(6 + bx + mn_major)).integers(
+        0, 65536, size=(bx, 64)).astype(np.uint16)
+    src = helpers.stored(tile, bool(mn_major), 16, 0xFFFF)
+    dsrc = helpers.to_dev(src)
+    dd = torch.zeros((bx // 16, 2, 64, 8), dtype=torch.int16, device="cuda")
+    assert hgemm.probe_fragments(mn_major, bx, dsrc.data_ptr(), src.shape[1], dd.data_ptr(),
+                                 helpers.stream_ptr()) == hgemm.OK
+    got = helpers.to_host(dd)
+    lane, e = np.arange(64), np.arange(8)
+    for f in range(bx // 16):
+        for sl in range(2):
+            want = tile[(16 * f + lane % 16)[:, None], (32 * sl + 8 * (lane // 16))[:, None] + e]
+            assert np.array_equal(got[f, sl], want), (f, sl)
