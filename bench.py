@@ -112,6 +112,92 @@ def oracle_table(only: int = 0) -> int:
     return 0
 
 
+def micro() -> int:
+    """Microbenchmarks behind the design choices (one JSON line each): matrix-
+    core issue rate per shape and operand data, LDS read throughput per
+    access pattern, L2 and HBM streaming, and the read path of the NN
+    operand at GEMM level (workload 3 computed four ways)."""
+    import numpy as np
+    import torch
+    from dense_half_precision_amd import hgemm, inputs
+    hgemm.lib()
+    lib = hgemm.lib()
+    sp = torch.cuda.current_stream().cuda_stream
+
+    def timed(f, n=10, warm=3):
+        for _ in range(warm):
+            assert f() == hgemm.OK
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            assert f() == hgemm.OK
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    def emit(d):
+        print(json.dumps(d), flush=True)
+
+    waves, iters = 1024, 4000
+    out = torch.empty(waves * 64, device="cuda")
+    clk = torch.zeros(2 * waves, dtype=torch.int64, device="cuda")
+    for shape in (0, 1):
+        for rnd in (0, 1):
+            ms = timed(lambda: lib.hgemm_probe_mfma_rate(shape, rnd, waves, iters, out.data_ptr(),
+                                                         clk.data_ptr(), sp))
+            c = clk.cpu().numpy().reshape(-1, 2)
+            mhz = float(np.median(c[:, 0] / c[:, 1]) * 100.0)  # real-time counter: 100 MHz
+            flop = waves * iters * 16 * (32768 if shape == 0 else 16384)
+            emit({"micro": "mfma_rate", "shape": "32x32x16" if shape == 0 else "16x16x32",
+                  "operands": "random" if rnd else "constant", "ms": round(ms, 4),
+                  "tflops": round(flop / ms / 1e9, 1), "sclk_mhz": round(mhz),
+                  "pct_of_clock_peak": round(100 * flop / ms / 1e9 / (256 * 4096 * mhz / 1e6), 1)})
+    names = {0: "lane-contiguous", 1: "baseline 32-row fragments, XOR", 2: "baseline, plain",
+             3: "baseline, XOR by row", 4: "production 16-row fragments, XOR",
+             5: "production 16-row fragments, plain", 6: "production transposing read, XOR",
+             7: "production transposing read, plain"}
+    wg, it = 512, 2000
+    lout = torch.empty(wg * 256, device="cuda")
+    for pat in range(8):
+        ms = timed(lambda: lib.hgemm_probe_lds_read(wg, it, pat, lout.data_ptr(), sp))
+        byts = wg * 256 * it * 16 * 16
+        emit({"micro": "lds_read", "pattern": pat, "what": names[pat], "ms": round(ms, 4),
+              "tb_per_s": round(byts / ms / 1e9, 2)})
+    # L2-to-CU streaming out of an L2-resident 4 MiB window (each workgroup's
+    # 64 KiB slides by 1 KiB per iteration), rows contiguous or 16 KiB apart
+    # (one K step of a K = 8192 operand panel)
+    window = 4 << 20
+    buf = torch.empty(window, dtype=torch.uint8, device="cuda")
+    for stride in (128, 16384):
+        for mode, what in ((0, "registers"), (1, "direct-to-LDS")):
+            wgs, its = 1024, 256
+            ms = timed(lambda: lib.hgemm_probe_l2_read(wgs, its, mode, buf.data_ptr(), window,
+                                                       stride, lout.data_ptr(), sp))
+            emit({"micro": "l2_stream", "row_stride": stride, "mode": what, "ms": round(ms, 4),
+                  "tb_per_s": round(wgs * its * 65536 / ms / 1e9, 2)})
+    w = inputs.workload(3)
+    A, B = inputs.operands(w)
+    dA = torch.from_numpy(A.view(np.int16)).cuda()
+    dB = torch.from_numpy(B.view(np.int16)).cuda()
+    dBt = torch.from_numpy(np.ascontiguousarray(B.T).view(np.int16)).cuda()
+    dC = torch.empty((w.M, w.N), dtype=torch.int16, device="cuda")
+    for name, fn, dB_ in (("tn_bf16_256x256x64", hgemm.hgemm_tn_ex, dBt),
+                          ("nn_bf16_256x256x64", hgemm.hgemm_nn_ex, dB),
+                          ("nn_bf16_256x256x64_plainlds", hgemm.hgemm_nn_ex, dB),
+                          ("rs_nn_bf16_256x256x64_xor", hgemm.hgemm_nn_ex, dB)):
+        k = hgemm.kernel_index(name)
+        ms = timed(lambda: fn(w.M, w.N, w.K, w.dtype, dA.data_ptr(), dB_.data_ptr(),
+                              dC.data_ptr(), sp, kernel=k), n=50, warm=10)
+        emit({"micro": "nn_read_path", "workload": w.name, "kernel": name,
+              "b_operand": "pre-transposed (Bt), 16-byte reads" if name.startswith("tn") else
+              ("register transpose" if name.startswith("rs") else "transposing LDS read"),
+              "ms": round(ms, 4), "tflops": round(w.flops / ms / 1e9, 1)})
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,11 +212,18 @@ def main() -> int:
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the GEMM, run a plain device copy of this many MiB "
                          "(reference point for scaling FETCH_SIZE/WRITE_SIZE counters)")
+    ap.add_argument("--micro", action="store_true",
+                    help="run the microbenchmarks behind the design choices and exit")
     ap.add_argument("--oracle-table", action="store_true",
                     help="time the CPU oracle on every workload (host only) and exit")
     args = ap.parse_args()
     if args.oracle_table:
         return oracle_table(args.workload if "--workload" in sys.argv else 0)
+    if args.micro:
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            return 2
+        return micro()
 
     if args.gpus != 1:
         print(f"bench.py: this HGEMM runs on one GPU; --gpus {args.gpus} is not supported "

@@ -1,7 +1,10 @@
 // probe.hip -- test-support kernels (declared in include/hgemm_probe.h): run
-// the MFMA wrapper and the LDS store/read addressing of the GEMM kernels in
-// isolation.
+// the GEMM kernels' building blocks in isolation (MFMA lane maps, LDS
+// placement and fragment reads, tile order) and measure the hardware rates
+// the design rests on (matrix-core issue rate and clock per shape and data,
+// LDS read throughput per access pattern, L2-to-CU streaming).
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "hgemm_probe.h"
@@ -123,6 +126,130 @@ __global__ __launch_bounds__(256) void probe_mfma_peak_kernel(int iters, float *
     const int w = blockIdx.x * 4 + (t >> 6);
     clocks[2 * w] = c1 - c0;      // shader clock cycles
     clocks[2 * w + 1] = r1 - r0;  // constant-rate real-time ticks
+  }
+}
+
+// Production fragment reads over one wave's 16 KiB quarter: 4 k-contiguous
+// 16-row fragments (rows of 128 bytes, one 16-byte read each) or, with the
+// transposing read, a 64 x 128 m/n-contiguous tile (rows of 256 bytes, two
+// 8-byte reads per fragment), with the XOR layout (XOR) or without.
+template <bool TR, bool XOR>
+__global__ __launch_bounds__(256) void probe_lds_frag_kernel(int iters, float *out) {
+  __shared__ __attribute__((aligned(1024))) char smem[65536];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int i = t; i < 65536 / 16; i += 256) ((u32x4 *)smem)[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  constexpr int L = XOR ? kLdsXor : kLdsPlain;
+  char *q = smem + wave * 16384;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  if constexpr (!TR) {
+    uint32_t off[2];
+    for (int sl = 0; sl < 2; ++sl) off[sl] = kmajor_frag_offset<L>(lane, sl);
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {  // fragment j % 8 of a 128-row block, slice j / 8
+        const u32x4 v = *(const u32x4 *)(q + (j & 7) * 16 * 128 + off[j >> 3]);
+        acc ^= v;
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    }
+  } else {
+    uint32_t off[8];
+    for (int f = 0; f < 8; ++f) off[f] = mnmajor_frag_offset<L>(lane, 16 * f, 256);
+    for (int i = 0; i < iters; ++i) {
+      // 16 fragments of 16 bytes per lane = 32 transposing reads, in groups of
+      // 8; the reads are not compiler-tracked, so each group ends in an
+      // explicit wait tied to all eight destinations
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        u32x2 v[8];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = 4 * jg + jj;
+          v[2 * jj] = lds_read_tr16(lds_addr(q + off[j & 7]), (j >> 3) * 32 * 256);
+          v[2 * jj + 1] = lds_read_tr16(lds_addr(q + off[j & 7]), ((j >> 3) * 32 + 4) * 256);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]));
+#pragma unroll
+        for (int r = 1; r < 8; ++r) asm volatile("" : "+v"(v[r]));
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          acc[0] ^= v[r][0];
+          acc[1] ^= v[r][1];
+        }
+      }
+    }
+  }
+  out[blockIdx.x * 256 + t] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+}
+
+// Matrix-core issue rate of one shape: each wave runs iters x 16 MFMAs over
+// 16 independent accumulators.  With RANDOM the operands are 8 + 8 registers
+// of pseudo-random FP16 values in (-1, 1): x changes from one MFMA to the
+// next and y every 16, so that consecutive MFMAs see different bits (as in a
+// GEMM); otherwise one constant pair.  The MFMAs are inline assembly with the
+// accumulators pinned to AGPRs and the operands to VGPRs: compiled from the
+// builtins, this loop picks up register moves between the MFMAs that would be
+// measured instead of the matrix core.  Each accumulator is reused 16 MFMAs
+// later, far past the instruction's latency.
+template <int SHAPE>
+__device__ __forceinline__ void mfma_pinned(f32x16 &acc, const u32x4 &a, const u32x4 &b) {
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+template <int SHAPE>
+__device__ __forceinline__ void mfma_pinned(f32x4 &acc, const u32x4 &a, const u32x4 &b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+template <int SHAPE, bool RANDOM>
+__global__ __launch_bounds__(256) void probe_mfma_rate_kernel(int iters, float *out,
+                                                              uint64_t *clocks) {
+  const int t = threadIdx.x;
+  u32x4 x[8], y[8];
+  uint32_t h = 0x9E3779B9u * (uint32_t)(t + 1);
+  for (int i = 0; i < 8; ++i)
+    for (int e = 0; e < 4; ++e) {
+      uint32_t w = 0x3C003C00u;  // 1.0, 1.0
+      if (RANDOM) {
+        h = h * 1664525u + 1013904223u;  // LCG: random sign and mantissa, exponent -1
+        w = (h & 0x83FF83FFu) | 0x38003800u;
+      }
+      x[i][e] = w;
+      y[i][e] = RANDOM ? (w ^ 0x80008000u) + (uint32_t)i : w;
+    }
+  using Acc = std::conditional_t<SHAPE == 0, f32x16, f32x4>;
+  constexpr int R = SHAPE == 0 ? 16 : 4;
+  Acc acc[16];
+  for (int j = 0; j < 16; ++j) acc[j] = Acc{};
+  // the compiler inserts no hazard wait states around inline assembly: let the
+  // zeroing writes of the accumulators settle before the first MFMA reads them
+  // (the empty statements pin the writes before the wait)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) asm volatile("" : "+a"(acc[j]));
+  // operands opaque to the compiler: held in VGPRs, never rebuilt in the loop
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(x[i]), "+v"(y[i]));
+  asm volatile("s_nop 7" ::: "memory");
+  const uint64_t c0 = clock64(), r0 = wall_clock64();
+  for (int it = 0; it < iters; it += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mfma_pinned<SHAPE>(acc[j], x[j & 7], y[u]);
+  }
+  // nor after it: wait out the last MFMAs' latency (256 wait states) before
+  // the accumulators are read
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("s_nop 15" ::: "memory");
+  const uint64_t c1 = clock64(), r1 = wall_clock64();
+  float s = 0.0f;
+  for (int j = 0; j < 16; ++j)
+    for (int r = 0; r < R; ++r) s += acc[j][r];
+  out[blockIdx.x * 256 + t] = s;
+  if (clocks != nullptr && (t & 63) == 0) {
+    const int w = blockIdx.x * 4 + (t >> 6);
+    clocks[2 * w] = c1 - c0;
+    clocks[2 * w + 1] = r1 - r0;
   }
 }
 
@@ -338,6 +465,21 @@ hgemm_status_t hgemm_probe_mfma_peak(int waves, int iters, float *out, uint64_t 
   return launched();
 }
 
+hgemm_status_t hgemm_probe_mfma_rate(int shape, int random, int waves, int iters, float *out,
+                                     uint64_t *clocks, void *stream) {
+  clear_error();
+  if ((shape != 0 && shape != 1) || (random != 0 && random != 1)) return HGEMM_ERR_INVALID_ARG;
+  if (waves <= 0 || waves % 4 != 0 || iters <= 0 || iters % 8 != 0 || !out)
+    return HGEMM_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 g(waves / 4), b(256);
+  if (shape == 0 && !random) hipLaunchKernelGGL((probe_mfma_rate_kernel<0, false>), g, b, 0, s, iters, out, clocks);
+  if (shape == 0 && random) hipLaunchKernelGGL((probe_mfma_rate_kernel<0, true>), g, b, 0, s, iters, out, clocks);
+  if (shape == 1 && !random) hipLaunchKernelGGL((probe_mfma_rate_kernel<1, false>), g, b, 0, s, iters, out, clocks);
+  if (shape == 1 && random) hipLaunchKernelGGL((probe_mfma_rate_kernel<1, true>), g, b, 0, s, iters, out, clocks);
+  return launched();
+}
+
 hgemm_status_t hgemm_probe_lds_read(int workgroups, int iters, int pattern, float *out,
                                     void *stream) {
   clear_error();
@@ -348,6 +490,10 @@ hgemm_status_t hgemm_probe_lds_read(int workgroups, int iters, int pattern, floa
     case 1: hipLaunchKernelGGL(probe_lds_read_kernel<1>, dim3(workgroups), dim3(256), 0, s, iters, out); break;
     case 2: hipLaunchKernelGGL(probe_lds_read_kernel<2>, dim3(workgroups), dim3(256), 0, s, iters, out); break;
     case 3: hipLaunchKernelGGL(probe_lds_read_kernel<3>, dim3(workgroups), dim3(256), 0, s, iters, out); break;
+    case 4: hipLaunchKernelGGL((probe_lds_frag_kernel<false, true>), dim3(workgroups), dim3(256), 0, s, iters, out); break;
+    case 5: hipLaunchKernelGGL((probe_lds_frag_kernel<false, false>), dim3(workgroups), dim3(256), 0, s, iters, out); break;
+    case 6: hipLaunchKernelGGL((probe_lds_frag_kernel<true, true>), dim3(workgroups), dim3(256), 0, s, iters, out); break;
+    case 7: hipLaunchKernelGGL((probe_lds_frag_kernel<true, false>), dim3(workgroups), dim3(256), 0, s, iters, out); break;
     default: return HGEMM_ERR_INVALID_ARG;
   }
   return launched();

@@ -91,6 +91,8 @@ def _lib() -> ctypes.CDLL:
     lib.hgemm_probe_lds_roundtrip.restype = i32
     lib.hgemm_probe_mfma_peak.argtypes = [i32, i32, vp, vp, vp]
     lib.hgemm_probe_mfma_peak.restype = i32
+    lib.hgemm_probe_mfma_rate.argtypes = [i32, i32, i32, i32, vp, vp, vp]
+    lib.hgemm_probe_mfma_rate.restype = i32
     lib.hgemm_probe_lds_read.argtypes = [i32, i32, i32, vp, vp]
     lib.hgemm_probe_lds_read.restype = i32
     lib.hgemm_probe_l2_read.argtypes = [i32, i32, i32, vp, ctypes.c_uint32, ctypes.c_uint32, vp, vp]

@@ -103,14 +103,34 @@ hgemm_status_t hgemm_probe_mfma_peak(int waves, int iters, float *out, uint64_t 
                                      void *stream);
 
 /*
+ * Matrix-core issue rate per shape and operand data: `waves` waves (in
+ * workgroups of 4) each issue `iters` x 16 (iters a multiple of 8) FP16
+ * MFMAs on 16 independent
+ * accumulators, shape 0 = 32x32x16 (32768 FLOP each), 1 = 16x16x32 (16384
+ * FLOP each); random 1: operands rotate over 8 + 8 registers of
+ * pseudo-random values in (-1, 1), as a GEMM's do, 0: one constant pair.
+ * The sustained clock under the board's power limit depends on both.
+ * out: waves*64 floats; clocks (may be NULL): per wave, shader-clock cycles
+ * and constant-rate real-time ticks (2*waves uint64).
+ */
+hgemm_status_t hgemm_probe_mfma_rate(int shape, int random, int waves, int iters, float *out,
+                                     uint64_t *clocks, void *stream);
+
+/*
  * LDS read throughput of one 16-byte-per-lane access pattern, over a
  * 64 KiB buffer per workgroup of 256 threads, `iters` x 16 reads per lane:
  *   pattern 0: lane-contiguous (lane l reads bytes 16*l .. of a 1 KiB row),
  *   pattern 1: the GEMM operand-fragment read with the XOR swizzle,
  *   pattern 2: the same read on plain (unswizzled) 128-byte rows,
- *   pattern 3: the same read with the chunk ^ (row & 7) swizzle.
- * Bytes read = workgroups * 256 * iters * 16 * 16.  out: workgroups*256
- * floats.
+ *   pattern 3: the same read with the chunk ^ (row & 7) swizzle
+ *   (patterns 1-3: the 32-row fragments of the register-staged baseline);
+ *   pattern 4: the production 16-row fragment read (k-contiguous operand)
+ *              with the XOR layout,  pattern 5: the same on plain rows,
+ *   pattern 6: the production transposing fragment read (two 8-byte
+ *              ds_read_b64_tr_b16 per 16 bytes) on 256-byte k-rows with the
+ *              XOR layout,  pattern 7: the same without it.
+ * Bytes read = workgroups * 256 * iters * 16 * 16 for every pattern.
+ * out: workgroups*256 floats.
  */
 hgemm_status_t hgemm_probe_lds_read(int workgroups, int iters, int pattern, float *out,
                                     void *stream);

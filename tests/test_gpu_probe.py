@@ -115,3 +115,30 @@ def test_operand_fragments(mn_major, bx):
         for sl in range(2):
             want = tile[(16 * f + lane % 16)[:, None], (32 * sl + 8 * (lane // 16))[:, None] + e]
             assert np.array_equal(got[f, sl], want), (f, sl)
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+@pytest.mark.parametrize("random", [0, 1])
+def test_mfma_rate_probe_runs(shape, random):
+    """The issue-rate probe launches and its sums and clocks are sane (the
+    throughput itself is measured by the bench's microbenchmark mode)."""
+    import torch
+    waves = 8
+    out = torch.full((waves * 64,), float("nan"), device="cuda")
+    clk = torch.zeros(2 * waves, dtype=torch.int64, device="cuda")
+    assert hgemm.lib().hgemm_probe_mfma_rate(shape, random, waves, 8, out.data_ptr(),
+                                             clk.data_ptr(), helpers.stream_ptr()) == hgemm.OK
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    c = clk.cpu().numpy().reshape(-1, 2)
+    assert (c[:, 0] > 0).all() and (c[:, 1] > 0).all()
+
+
+@pytest.mark.parametrize("pattern", range(8))
+def test_lds_read_probe_runs(pattern):
+    import torch
+    out = torch.full((2 * 256,), float("nan"), device="cuda")
+    assert hgemm.lib().hgemm_probe_lds_read(2, 3, pattern, out.data_ptr(),
+                                            helpers.stream_ptr()) == hgemm.OK
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()

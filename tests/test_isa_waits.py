@@ -22,6 +22,25 @@ def kernels(tmp_path_factory):
     return ks
 
 
+@pytest.fixture(scope="module")
+def probe_kernels(tmp_path_factory):
+    out = tmp_path_factory.mktemp("asm") / "probe.s"
+    asm = open(hbuild.asm("probe.hip", str(out))).read()
+    ks = isa_waits.kernel_bodies(asm, "_Z")
+    assert ks
+    return ks
+
+
+def test_probe_kernels_no_early_use(probe_kernels):
+    """The probes that run the transposing read (inline assembly) too."""
+    tr = 0
+    for name, lines in probe_kernels.items():
+        tr += sum("ds_read_b64_tr_b16" in l for l in lines)
+        bad = isa_waits.check_kernel(lines)
+        assert not bad, f"{name}: {bad[:5]}"
+    assert tr > 0
+
+
 def test_no_early_use_of_lds_reads(kernels):
     tr = 0
     for name, lines in kernels.items():
