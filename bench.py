@@ -198,6 +198,70 @@ def micro() -> int:
     return 0
 
 
+TAIL_SHAPES = [  # (layout, dtype, M, N, K): tiles of 256 x 256 that leave a partial round
+    ("tn", "f16", 6144, 6144, 6144), ("nn", "bf16", 6144, 6144, 6144),
+    ("tn", "f16", 7168, 7168, 7168), ("tn", "f16", 4352, 4352, 4096),
+    ("nn", "bf16", 1536, 1536, 16384), ("tn", "f16", 512, 512, 65536),
+    ("tn", "f16", 1024, 8192, 8192)]
+
+
+def tail() -> int:
+    """K split of the tail (one JSON line per shape): the automatic choice
+    without a workspace, with one (hgemm_gemm_ws), and torch.mm (the vendor
+    library) on the same operands; the three are timed in alternation so that
+    clock drift under the power cap falls on all of them alike."""
+    import numpy as np
+    import torch
+    from dense_half_precision_amd import hgemm, inputs
+    sp = torch.cuda.current_stream().cuda_stream
+    for lay, dt, M, N, K in TAIL_SHAPES:
+        opB = hgemm.OP_T if lay == "tn" else hgemm.OP_N
+        A = inputs.draw((M, K), dt, "normal", 1)
+        B = inputs.draw((N, K) if lay == "tn" else (K, N), dt, "normal", 2)
+        dA = torch.from_numpy(A.view(np.int16)).cuda()
+        dB = torch.from_numpy(B.view(np.int16)).cuda()
+        dC = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        ldb = K if lay == "tn" else N
+        need = hgemm.gemm_ws_size(hgemm.OP_N, opB, M, N, K, dt)
+        ws = torch.empty(max(need, 16) // 4, dtype=torch.float32, device="cuda")
+        args = (hgemm.OP_N, opB, M, N, K, dt, 1.0, dA.data_ptr(), K, dB.data_ptr(), ldb, 0.0,
+                dC.data_ptr(), N)
+        tdt = torch.float16 if dt == "f16" else torch.bfloat16
+        a, b = dA.view(tdt), dB.view(tdt)
+        variants = {
+            "unsplit": lambda: hgemm.hgemm_gemm(*args, sp),
+            "split": lambda: hgemm.hgemm_gemm_ws(*args, ws.data_ptr(), need, sp),
+            "torch.mm": (lambda: torch.mm(a, b.t())) if lay == "tn" else (lambda: torch.mm(a, b)),
+        }
+        times = {k: [] for k in variants}
+        for _ in range(5):
+            f = variants["unsplit"]
+            assert f() == hgemm.OK and variants["split"]() == hgemm.OK
+        for _ in range(3):
+            for name, f in variants.items():
+                for _ in range(3):
+                    f()
+                torch.cuda.synchronize()
+                for _ in range(10):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    f()
+                    e1.record()
+                    e1.synchronize()
+                    times[name].append(e0.elapsed_time(e1))
+        flop = 2.0 * M * N * K
+        ms = {k: float(np.median(v)) for k, v in times.items()}
+        tiles = -(-M // 256) * -(-N // 256)
+        print(json.dumps({"tail": f"{lay} {dt} {M}x{N}x{K}", "tiles_256": tiles,
+                          "tail_tiles": tiles % 256, "workspace_mib": round(need / 2**20, 2),
+                          "segments": need // (262144 * (tiles % 256)) if need else 0,
+                          **{f"{k}_tflops": round(flop / v / 1e9, 1) for k, v in ms.items()},
+                          "split_vs_unsplit": round(ms["unsplit"] / ms["split"], 3),
+                          "split_vs_torch": round(ms["torch.mm"] / ms["split"], 3)}), flush=True)
+        del dA, dB, dC, ws
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,11 +278,18 @@ def main() -> int:
                          "(reference point for scaling FETCH_SIZE/WRITE_SIZE counters)")
     ap.add_argument("--micro", action="store_true",
                     help="run the microbenchmarks behind the design choices and exit")
+    ap.add_argument("--tail", action="store_true",
+                    help="K split of the tail vs the unsplit choice and torch.mm, per shape")
     ap.add_argument("--oracle-table", action="store_true",
                     help="time the CPU oracle on every workload (host only) and exit")
     args = ap.parse_args()
     if args.oracle_table:
         return oracle_table(args.workload if "--workload" in sys.argv else 0)
+    if args.tail:
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            return 2
+        return tail()
     if args.micro:
         if args.gpus != 1:
             print("bench.py: one GPU only", file=sys.stderr)

@@ -41,6 +41,14 @@ struct GemmArgs {
   float alpha, beta;  // C = alpha * A B + beta * C; beta == 0: C is not read
   int group_m;        // >= 1
   int xcd_remap;      // 0 or 1
+  // The launch covers positions tile_begin .. of the grouped tile order with
+  // `grid` workgroups.  sk_split == 0: one tile per workgroup, whole K.
+  // sk_split = S >= 2: sk_tiles tiles, each split into S K-segments, one
+  // workgroup per segment, whose FP32 partial sums go to `ws` (the fixup
+  // kernel adds them up and writes C).
+  int tile_begin, grid;
+  int sk_split, sk_tiles;
+  float *ws;
 };
 
 // Scheduling hints for one phase: after each of the NMF matrix-core
@@ -137,23 +145,41 @@ __host__ __device__ __forceinline__ uint32_t mnmajor_frag_offset(int lane, int x
   return k * rowb + c * 16 + (i & 1) * 8;
 }
 
-// Map the dispatch index to (tile_m, tile_n).
+// Position of workgroup `pid` in the tile sequence of a launch of `grid`
+// workgroups.  Workgroup i runs on XCD i % 8; with the remap, XCD x receives
+// the contiguous positions [x*per, (x+1)*per) (per = grid / 8), so that the
+// tiles resident on one XCD are neighbours in the grouped order below and
+// share A and B panels in its L2.  Positions past 8*per keep their index.
+__host__ __device__ __forceinline__ int xcd_position(int pid, int grid, int xcd_remap) {
+  if (xcd_remap) {
+    const int per = grid >> 3;
+    if (pid < (per << 3)) return (pid & 7) * per + (pid >> 3);
+  }
+  return pid;
+}
+
+// Tile at position v of the grouped order: groups of group_m tile rows, each
+// walked column by column (down the group's rows first).
+__host__ __device__ __forceinline__ void tile_of(int v, int tiles_m, int tiles_n, int group_m,
+                                                 int &tm, int &tn) {
+  const int width = group_m * tiles_n;
+  const int g = v / width;
+  const int first_m = g * group_m;
+  const int gsz = (tiles_m - first_m < group_m) ? tiles_m - first_m : group_m;
+  const int in = v - g * width;
+  tm = first_m + in % gsz;
+  tn = in / gsz;
+}
+
+// Workgroups of the K-split fixup per tile: a BM x BN tile's FP32 partial
+// sums are BM*BN/256 chunks of 1 KiB, 16 chunks a workgroup.
+__host__ __device__ constexpr int fixup_parts(int bm, int bn) { return bm * bn / 4096; }
+
+// Dispatch index -> (tile_m, tile_n) for a launch over the whole tile grid.
 __host__ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n,
                                                      int group_m, int xcd_remap, int &tm,
                                                      int &tn) {
-  const int total = tiles_m * tiles_n;
-  if (xcd_remap) {
-    // workgroup i runs on XCD i % 8; give XCD x the ids [x*per, (x+1)*per)
-    const int per = total >> 3;
-    if (pid < (per << 3)) pid = (pid & 7) * per + (pid >> 3);
-  }
-  const int width = group_m * tiles_n;
-  const int g = pid / width;
-  const int first_m = g * group_m;
-  const int gsz = (tiles_m - first_m < group_m) ? tiles_m - first_m : group_m;
-  const int in = pid - g * width;
-  tm = first_m + in % gsz;
-  tn = in / gsz;
+  tile_of(xcd_position(pid, tiles_m * tiles_n, xcd_remap), tiles_m, tiles_n, group_m, tm, tn);
 }
 
 }  // namespace hgemm

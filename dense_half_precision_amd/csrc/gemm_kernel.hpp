@@ -82,7 +82,98 @@ struct TileCfg {
   static_assert(LDS == kLdsXor || LDS == kLdsPlain, "layouts of this kernel");
 };
 
-template <class T, int LAYOUT, int DT>
+// Epilogue of a BM x BN tile whose FP32 sums a workgroup holds in acc (wave
+// w: block (w/2, w%2) of (BM/2) x (BN/2); lane l, tile (i, j): C[m][n .. n+3],
+// m = block row + 16i + l%16, n = block column + 16j + 4*(l/16)).
+// C = alpha * acc + beta * C, rounded once to the output type; with alpha ==
+// 1 and beta == 0 the sums are converted as they are and C is not read.
+template <class T, int DT>
+__device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T::FM][T::FN],
+                                           char *smem, int m0, int n0, int wave, int lane) {
+  constexpr int FM = T::FM, FN = T::FN;
+  const int M = args.M, N = args.N, ldc = args.ldc;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int wm0 = m0 + wm * T::WTM, wn0 = n0 + wn * T::WTN;
+  const float alpha = args.alpha, beta = args.beta;
+  // packed output of tile (i, j) for this lane
+  auto out2 = [&](auto GEN_, int i, int j) {
+    constexpr bool GEN = decltype(GEN_)::value;
+    float x[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+    if constexpr (GEN) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] *= alpha;
+      if (beta != 0.0f) {
+        const int m = wm0 + i * 16 + (lane & 15), n = wn0 + j * 16 + 4 * (lane >> 4);
+        if (m < M && n < N) {
+          const u32x2 c = *(const u32x2 *)(args.C + (size_t)m * ldc + n);
+          float c0, c1, c2, c3;
+          unpack2<DT>(c[0], c0, c1);
+          unpack2<DT>(c[1], c2, c3);
+          x[0] = __builtin_fmaf(beta, c0, x[0]);
+          x[1] = __builtin_fmaf(beta, c1, x[1]);
+          x[2] = __builtin_fmaf(beta, c2, x[2]);
+          x[3] = __builtin_fmaf(beta, c3, x[3]);
+        }
+      }
+    }
+    u32x2 v;
+    v[0] = pack2<DT>(x[0], x[1]);
+    v[1] = pack2<DT>(x[2], x[3]);
+    return v;
+  };
+  // In the general form the reads of the old C go one row block at a time
+  // (the empty asm keeps later rows' reads from being hoisted), so that their
+  // registers do not pile up next to the accumulators.
+  auto epilogue = [&](auto GEN_) {
+    constexpr bool GEN = decltype(GEN_)::value;
+    if constexpr (T::EPI) {
+      __builtin_amdgcn_s_waitcnt(0);  // no load still writing LDS, no read pending
+      wg_barrier();                   // every wave is done with the pipeline stages
+      char *cw = smem + wave * (T::WTM * T::CROW);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          *(u32x2 *)(cw + (i * 16 + (lane & 15)) * T::CROW + (j * 16 + 4 * (lane >> 4)) * 2) =
+              out2(GEN_, i, j);
+        if constexpr (GEN) asm volatile("" ::: "memory");
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+      // each row of the wave block is WTN*2 bytes = WTN/8 lanes of 16 bytes
+      constexpr int LPR = T::WTN / 8, RPI = 64 / LPR;
+#pragma unroll
+      for (int r = 0; r < T::WTM / RPI; ++r) {
+        const int row = r * RPI + lane / LPR, col = 8 * (lane % LPR);
+        const u32x4 v = *(const u32x4 *)(cw + row * T::CROW + col * 2);
+        const int m = wm0 + row, n = wn0 + col;
+        if (m < M && n < N) *(u32x4 *)(args.C + (size_t)m * ldc + n) = v;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = wm0 + i * 16 + (lane & 15);
+        if (m < M) {
+          uint16_t *crow = args.C + (size_t)m * ldc;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int n = wn0 + j * 16 + 4 * (lane >> 4);
+            if (n < N) *(u32x2 *)(crow + n) = out2(GEN_, i, j);
+          }
+        }
+        if constexpr (GEN) asm volatile("" ::: "memory");
+      }
+    }
+  };
+  if (alpha == 1.0f && beta == 0.0f)
+    epilogue(std::false_type{});
+  else
+    epilogue(std::true_type{});
+}
+
+// SPLIT: the workgroup computes one K segment of a tile and writes FP32
+// partial sums to the workspace (a separate instantiation, so that the
+// data-parallel kernel carries none of the segment bookkeeping in registers).
+template <class T, int LAYOUT, int DT, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
   constexpr int FM = T::FM, FN = T::FN, NMF = T::NMF;
@@ -104,14 +195,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   const int M = args.M, N = args.N, K = args.K;
   const int lda = args.lda, ldb = args.ldb;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  // This workgroup's tile and K steps: position `pos` of the launch; with a K
+  // split, tile pos % sk_tiles of the launch's range, segment pos / sk_tiles,
+  // steps [seg*KT/S, (seg+1)*KT/S).
+  const int KT_all = (K + BK - 1) / BK;
+  const int pos = __builtin_amdgcn_readfirstlane(xcd_position(blockIdx.x, args.grid, args.xcd_remap));
+  const int S = SPLIT ? args.sk_split : 1;
+  const int seg = SPLIT ? pos / args.sk_tiles : 0;
   int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, args.group_m, args.xcd_remap, tm, tn);
-  // tile_coords divides on the vector unit; the tile origin is uniform and is
+  tile_of(args.tile_begin + (SPLIT ? pos % args.sk_tiles : pos), tiles_m, tiles_n, args.group_m,
+          tm, tn);
+  // the tile order divides on the vector unit; the results are uniform and are
   // moved to scalar registers explicitly, so that the buffer descriptors built
-  // from it stay scalar (a descriptor held in vector registers turns every
+  // from them stay scalar (a descriptor held in vector registers turns every
   // load into a per-lane loop)
   const int m0 = __builtin_amdgcn_readfirstlane(tm * BM);
   const int n0 = __builtin_amdgcn_readfirstlane(tn * BN);
+  const int s_begin = SPLIT ? __builtin_amdgcn_readfirstlane(seg * KT_all / S) : 0;
+  const int s_end = SPLIT ? __builtin_amdgcn_readfirstlane((seg + 1) * KT_all / S) : KT_all;
+  const int K_end = SPLIT ? min(K, s_end * BK) : K;  // K limit of this workgroup's loads
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -152,16 +254,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   auto b_base = [&](int s) { return (uint32_t)(T::B_BASE + (s & 1) * T::B_STAGE); };
 
   // Buffer resource of one operand for the K step starting at k0: rows past
-  // the tile edge (k-contiguous) or k-rows past K (m/n-contiguous) fall
-  // outside it and read as zero.
+  // the tile edge (k-contiguous) or k-rows past this workgroup's K range
+  // (m/n-contiguous) fall outside it and read as zero, and so does every step
+  // past the range (no traffic for the loads the pipeline runs ahead).
   // (One descriptor built from selected base and size: descriptors merged from
   // branches lose their uniformity and end up in a per-lane loop.)
   auto rsrc_of = [&](bool mn, const uint16_t *panel, int ld, int rows, int k0) {
-    const int krem = K - k0;
+    const int krem = K_end - k0;
     const uint16_t *base = mn ? panel + (size_t)k0 * ld : panel + k0;
     const uint32_t bytes = krem <= 0 ? 0u
                            : mn      ? (uint32_t)(min(krem, BK) * ld) * 2u
-                                     : (uint32_t)((rows - 1) * ld + K - k0) * 2u;
+                                     : (uint32_t)((rows - 1) * ld + K_end - k0) * 2u;
     return make_rsrc(base, bytes);
   };
   __amdgpu_buffer_rsrc_t rs_a, rs_b;
@@ -180,6 +283,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   // feeding each load would sit in the MFMA stream and stall it.
   const int tail = (K % BK) ? (K - 1) / BK : -1;
   auto mask_tail = [&]() {
+    // (a side effect keeps this a branch: executed as selects on every step it
+    // would sit in the MFMA stream and hold both offset sets in registers)
+    asm volatile("" ::: "memory");
     const int kr = K - tail * BK;
     if constexpr (!A_MN) {
 #pragma unroll
@@ -268,23 +374,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
-  const int KT = (K + BK - 1) / BK;
+  // steps are counted from s_begin (stage ring positions) and loaded at
+  // absolute k = (s_begin + step) * BK; `tail` is an absolute step index
+  const int KT = s_end - s_begin;
 
   // ---- prologue: A of steps 0, 1 and B of step 0 in flight; slice 0 read ----
-  if (tail == 0) mask_tail();
-  prep_a(0);
+  if (tail == s_begin) mask_tail();
+  prep_a(s_begin);
 #pragma unroll
   for (int i = 0; i < SEG_A; ++i) load_a(a_base(0), i);
-  prep_b(0);
+  prep_b(s_begin);
 #pragma unroll
   for (int i = 0; i < SEG_B; ++i) load_b(b_base(0), i);
-  if (tail == 1) mask_tail();
-  prep_a(1);
+  if (tail == s_begin + 1) mask_tail();
+  prep_a(s_begin + 1);
 #pragma unroll
   for (int i = 0; i < SEG_A; ++i) load_a(a_base(1), i);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(SEG_A, 0));
   wg_barrier();
-  prep_b(1);
+  prep_b(s_begin + 1);
 #pragma unroll
   for (int q = 0; q < NR; ++q) {
     read_op(I0{}, a_base(0), b_base(0), 0, q);
@@ -294,11 +402,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
 
   // ---- main loop -------------------------------------------------------------
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 2 == tail) mask_tail();  // loads of steps kt+2 on are issued below
+    if (s_begin + kt + 2 == tail) mask_tail();  // loads of steps kt+2 on are issued below
     const uint32_t ca = a_base(kt), cb = b_base(kt);
     const uint32_t na = a_base(kt + 1), nb = b_base(kt + 1);
     // X: slice 0; read slice 1; A of step kt+2 into the stage step kt-1 used
-    prep_a(kt + 2);
+    prep_a(s_begin + kt + 2);
     const uint32_t la = a_base(kt + 2);
     wait_set(I0{});
 #pragma unroll
@@ -323,7 +431,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(SEG_A, 0));
     wg_barrier();
     // Z: second half of slice 1; read slice 0 of step kt+1; B of step kt+2
-    prep_b(kt + 2);
+    prep_b(s_begin + kt + 2);
     const uint32_t lb = b_base(kt + 2);
 #pragma unroll
     for (int t = NMF / 2; t < NMF; ++t) {
@@ -352,86 +460,95 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   }
 
   // ---- epilogue --------------------------------------------------------------
-  // lane holds, for tile (i, j): C[m][n .. n+3], m = wave row + 16i + lane%16,
-  // n = wave column + 16j + 4*(lane/16).  C = alpha * acc + beta * C, rounded
-  // once to the output type; with alpha == 1 and beta == 0 the FP32 sums are
-  // converted as they are and C is not read.
-  const int ldc = args.ldc;
-  const int wm0 = m0 + wm * T::WTM, wn0 = n0 + wn * T::WTN;
+  if constexpr (SPLIT) {
+    // a K segment: its FP32 sums go to workspace slot `pos`, each wave's block
+    // in lane order (16-byte stores, 1 KiB per instruction); the fixup kernel
+    // adds the segments of the tile in order and writes C
+    float *slot = args.ws + ((size_t)pos * 4 + wave) * (FM * FN * 256);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) *(f32x4 *)(slot + ((i * FN + j) * 64 + lane) * 4) = acc[i][j];
+  } else {
+    store_tile<T, DT>(args, acc, smem, m0, n0, wave, lane);
+  }
+}
+
+
+// Second half of a K-split launch: the S FP32 partial sums of each split tile
+// are added in segment order (so the result does not depend on which segment
+// finished first) and written to C with alpha and beta, rounded once.  A
+// tile's partial sums are 4*FM*FN chunks of 1 KiB (wave block, then MFMA tile
+// (i, j); one accumulator quad per lane); workgroup b handles the 16 chunks
+// 16*(b % P) .. of split tile b / P, each thread 4 chunks of one lane, with the
+// loads of four segments in flight before they are added (the sums are
+// bandwidth work: few registers a lane, many loads outstanding).
+template <class T, int DT>
+__global__ __launch_bounds__(256) void gemm_sk_fixup(GemmArgs args) {
+  constexpr int FM = T::FM, FN = T::FN;
+  constexpr int CHUNKS = 4 * FM * FN;
+  constexpr int P = fixup_parts(T::BM, T::BN);
+  static_assert(CHUNKS == 16 * P, "16 chunks a workgroup");
+  constexpr int SLOT = CHUNKS * 256;  // floats of one segment's partial sums
+  const int M = args.M, N = args.N, ldc = args.ldc;
+  const int tiles_m = (M + T::BM - 1) / T::BM, tiles_n = (N + T::BN - 1) / T::BN;
+  const int tile = blockIdx.x / P, part = blockIdx.x % P;
+  int tm, tn;
+  tile_of(args.tile_begin + tile, tiles_m, tiles_n, args.group_m, tm, tn);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c0 = part * 16 + wave * 4;  // this thread's chunks c0 .. c0+3
+  const float *src = args.ws + (size_t)tile * SLOT + (size_t)c0 * 256 + lane * 4;
+  const size_t seg_stride = (size_t)args.sk_tiles * SLOT;
+  const int S = args.sk_split;
+  f32x4 acc[4] = {};
+  int sg = 0;
+  for (; sg + 4 <= S; sg += 4) {
+    f32x4 p[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) p[b][c] = *(const f32x4 *)(src + (sg + b) * seg_stride + c * 256);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] += p[b][c];
+  }
+  for (; sg < S; ++sg) {
+    f32x4 p[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) p[c] = *(const f32x4 *)(src + sg * seg_stride + c * 256);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] += p[c];
+  }
   const float alpha = args.alpha, beta = args.beta;
-  // packed output of tile (i, j) for this lane
-  auto out2 = [&](auto GEN_, int i, int j) {
-    constexpr bool GEN = decltype(GEN_)::value;
-    float x[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-    if constexpr (GEN) {
+  const bool plain = alpha == 1.0f && beta == 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int ch = c0 + c, w = ch / (FM * FN), ij = ch % (FM * FN);
+    const int m = tm * T::BM + (w >> 1) * T::WTM + (ij / FN) * 16 + (lane & 15);
+    const int n = tn * T::BN + (w & 1) * T::WTN + (ij % FN) * 16 + 4 * (lane >> 4);
+    if (m >= M || n >= N) continue;  // N % 8 == 0: n < N covers n .. n+3
+    uint16_t *cp = args.C + (size_t)m * ldc + n;
+    float x[4] = {acc[c][0], acc[c][1], acc[c][2], acc[c][3]};
+    if (!plain) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] *= alpha;
       if (beta != 0.0f) {
-        const int m = wm0 + i * 16 + (lane & 15), n = wn0 + j * 16 + 4 * (lane >> 4);
-        if (m < M && n < N) {
-          const u32x2 c = *(const u32x2 *)(args.C + (size_t)m * ldc + n);
-          float c0, c1, c2, c3;
-          unpack2<DT>(c[0], c0, c1);
-          unpack2<DT>(c[1], c2, c3);
-          x[0] = __builtin_fmaf(beta, c0, x[0]);
-          x[1] = __builtin_fmaf(beta, c1, x[1]);
-          x[2] = __builtin_fmaf(beta, c2, x[2]);
-          x[3] = __builtin_fmaf(beta, c3, x[3]);
-        }
+        const u32x2 old = *(const u32x2 *)cp;
+        float c0f, c1f, c2f, c3f;
+        unpack2<DT>(old[0], c0f, c1f);
+        unpack2<DT>(old[1], c2f, c3f);
+        x[0] = __builtin_fmaf(beta, c0f, x[0]);
+        x[1] = __builtin_fmaf(beta, c1f, x[1]);
+        x[2] = __builtin_fmaf(beta, c2f, x[2]);
+        x[3] = __builtin_fmaf(beta, c3f, x[3]);
       }
     }
     u32x2 v;
     v[0] = pack2<DT>(x[0], x[1]);
     v[1] = pack2<DT>(x[2], x[3]);
-    return v;
-  };
-  // In the general form the reads of the old C go one row block at a time
-  // (the empty asm keeps later rows' reads from being hoisted), so that their
-  // registers do not pile up next to the accumulators.
-  auto epilogue = [&](auto GEN_) {
-    constexpr bool GEN = decltype(GEN_)::value;
-    if constexpr (T::EPI) {
-      __builtin_amdgcn_s_waitcnt(0);  // no load still writing LDS, no read pending
-      wg_barrier();                   // every wave is done with the pipeline stages
-      char *cw = smem + wave * (T::WTM * T::CROW);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          *(u32x2 *)(cw + (i * 16 + (lane & 15)) * T::CROW + (j * 16 + 4 * (lane >> 4)) * 2) =
-              out2(GEN_, i, j);
-        if constexpr (GEN) asm volatile("" ::: "memory");
-      }
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-      // each row of the wave block is WTN*2 bytes = WTN/8 lanes of 16 bytes
-      constexpr int LPR = T::WTN / 8, RPI = 64 / LPR;
-#pragma unroll
-      for (int r = 0; r < T::WTM / RPI; ++r) {
-        const int row = r * RPI + lane / LPR, col = 8 * (lane % LPR);
-        const u32x4 v = *(const u32x4 *)(cw + row * T::CROW + col * 2);
-        const int m = wm0 + row, n = wn0 + col;
-        if (m < M && n < N) *(u32x4 *)(args.C + (size_t)m * ldc + n) = v;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int m = wm0 + i * 16 + (lane & 15);
-        if (m < M) {
-          uint16_t *crow = args.C + (size_t)m * ldc;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int n = wn0 + j * 16 + 4 * (lane >> 4);
-            if (n < N) *(u32x2 *)(crow + n) = out2(GEN_, i, j);
-          }
-        }
-        if constexpr (GEN) asm volatile("" ::: "memory");
-      }
-    }
-  };
-  if (alpha == 1.0f && beta == 0.0f)
-    epilogue(std::false_type{});
-  else
-    epilogue(std::true_type{});
+    *(u32x2 *)cp = v;
+  }
 }
 
 }  // namespace hgemm

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <algorithm>
+
 #include "hgemm.h"
 #include "gemm_kernel.hpp"
 #include "gemm_regstage.hpp"
@@ -22,20 +24,23 @@ struct KernelEntry {
   const char *name;
   int layout, dtype, bm, bn, bk, lds, default_group_m;
   bool production;  // candidate of the automatic choice
-  bool general;     // honours leading dimensions, alpha and beta
+  bool general;     // honours leading dimensions, alpha, beta and K splits
   kernel_fn fn;
+  kernel_fn split_fn;  // one K segment of a tile into the workspace (general kernels)
+  kernel_fn fixup;     // adds the K segments of split tiles (general kernels)
 };
 
 template <class T, int LAYOUT, int DT>
 constexpr KernelEntry entry(const char *name, int group_m, bool production) {
   return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, production, true,
-                     &gemm_kernel<T, LAYOUT, DT>};
+                     &gemm_kernel<T, LAYOUT, DT, false>, &gemm_kernel<T, LAYOUT, DT, true>,
+                     &gemm_sk_fixup<T, DT>};
 }
 // the register-staged baseline assumes packed TN/NN operands, alpha 1, beta 0
 template <class T, int LAYOUT, int DT>
 constexpr KernelEntry rs_entry(const char *name, int group_m) {
   return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, false, false,
-                     &regstage_kernel<T, LAYOUT, DT>};
+                     &regstage_kernel<T, LAYOUT, DT>, nullptr, nullptr};
 }
 
 using T256 = TileCfg<256, 256>;
@@ -107,27 +112,101 @@ int find_kernel(int layout, int dtype, int bm) {
   return -1;
 }
 
-// Automatic choice: the tile size with the least estimated time, taken as
-// (waves of workgroups over the 256 CUs, one workgroup per CU) x (time of
-// one tile), a tile's time being its area over the per-CU throughput of that
-// tile size at full occupancy, measured relative to the 256 x 256 kernel
-// (128: 0.8, 64: 0.5).  Ties go to the larger tile.
-int auto_kernel(int layout, int dtype, int64_t M, int64_t N) {
-  constexpr int64_t kCUs = 256;
-  const int sizes[3] = {256, 128, 64};
-  const int64_t rate10[3] = {10, 8, 5};  // relative throughput x 10
-  int best = 256;
-  int64_t best_cost = -1;
-  for (int i = 0; i < 3; ++i) {
-    const int64_t t = sizes[i];
-    const int64_t tiles = ((M + t - 1) / t) * ((N + t - 1) / t);
-    const int64_t cost = ((tiles + kCUs - 1) / kCUs) * t * t * 40 / rate10[i];
-    if (best_cost < 0 || cost < best_cost) {
-      best_cost = cost;
-      best = sizes[i];
+// Estimated times, in units of one 256 x 256 x 64 tile step at full rate
+// (about 1.3 us on MI355X): a launch of square tiles of size t runs
+// ceil(tiles / 256 CUs) waves of one workgroup per CU, each tile taking
+// KT * (t/256)^2 / rate_t units, rate_t the per-CU throughput of that tile size
+// at full occupancy relative to the 256 kernel (128: 0.8, 64: 0.5, measured).
+// Cost model of the automatic choice, in units of one K step of a 256 x 256
+// tile on every CU at once (about 1.3 us on this chip), fitted to measured
+// times of the kernels below over square and skinny shapes.
+constexpr int64_t kCUs = 256;
+const int kSizes[3] = {256, 128, 64};
+const double kRate[3] = {1.0, 0.8, 0.5};  // sustained rate relative to the 256 x 256 tile
+constexpr double kTileFixed = 4.0;        // prologue and epilogue of a tile, in K steps
+constexpr double kSplitFixed = 6.9;       // the fixup launch and the wait between launches
+constexpr double kSplitDrain = 5.0;       // the whole-round launch draining before the tail
+constexpr double kSlotCost = 0.055;       // one 256 KiB partial sum written and read back
+constexpr int kMaxAutoSplit = 64;
+constexpr int64_t kMaxSlots = 1024;       // 256 MiB of partial sums at most
+
+double dp_cost(int i, int64_t M, int64_t N, int64_t KT) {
+  const int64_t t = kSizes[i];
+  const int64_t tiles = ((M + t - 1) / t) * ((N + t - 1) / t);
+  return (double)((tiles + kCUs - 1) / kCUs) * ((double)KT + kTileFixed) * (double)(t * t) /
+         65536.0 / kRate[i];
+}
+
+// Automatic choice without a K split: the tile size with the least estimated
+// time; ties go to the larger tile.
+int auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K) {
+  const int64_t KT = K > 0 ? (K + 63) / 64 : 1;
+  int best = 0;
+  for (int i = 1; i < 3; ++i)
+    if (dp_cost(i, M, N, KT) < dp_cost(best, M, N, KT)) best = i;
+  return find_kernel(layout, dtype, kSizes[best]);
+}
+
+// K split of the last, partial round of 256 x 256 tiles (the tail): the
+// tiles that do not fill a round of the 256 CUs are each cut into S K
+// segments run side by side, whose FP32 partial sums (BM*BN*4 bytes a
+// segment) a second kernel adds in order.
+struct Plan {
+  int kidx = -1;
+  int split = 0;         // 0: no split
+  int64_t dp_tiles = 0;  // tiles of the whole rounds, computed without a split
+  int64_t sk_tiles = 0;  // tail tiles, each split into `split` segments
+  size_t ws_bytes = 0;
+  double cost = 0.0;
+};
+
+double split_cost(int64_t full_rounds, int64_t tail, int64_t KT, int64_t S) {
+  const int64_t waves = (tail * S + kCUs - 1) / kCUs;
+  return (double)full_rounds * ((double)KT + kTileFixed) +
+         (double)waves * ((double)((KT + S - 1) / S) + kTileFixed) + kSplitFixed +
+         kSlotCost * (double)(tail * S) + (full_rounds > 0 ? kSplitDrain : 0.0);
+}
+
+// split > 0: that many segments; split == 0: the number with the least
+// estimated time.  No plan (split 0) when there is no tail or too few K steps.
+Plan split_plan(int layout, int dtype, int64_t M, int64_t N, int64_t K, int split) {
+  Plan p;
+  const int64_t KT = (K + 63) / 64;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t tail = tiles % kCUs, full = tiles / kCUs;
+  if (tail == 0 || KT < 2) return p;
+  int64_t S = split;
+  if (split <= 0) {
+    S = 0;
+    double best = 0.0;
+    for (int64_t s = 2; s <= std::min<int64_t>(KT, kMaxAutoSplit) && tail * s <= kMaxSlots; ++s) {
+      const double c = split_cost(full, tail, KT, s);
+      if (S == 0 || c < best) S = s, best = c;
     }
   }
-  return find_kernel(layout, dtype, best);
+  if (S < 2 || S > KT || tail * S > (int64_t(1) << 20)) return p;
+  p.kidx = find_kernel(layout, dtype, 256);
+  p.split = (int)S;
+  p.sk_tiles = tail;
+  p.dp_tiles = tiles - tail;
+  p.ws_bytes = (size_t)tail * (size_t)S * 256 * 256 * 4;
+  p.cost = split_cost(full, tail, KT, S);
+  return p;
+}
+
+// The plan of a call: the automatic tile choice, or the split schedule when a
+// large enough workspace is given and it is estimated faster (or forced).
+Plan choose(int layout, int dtype, int64_t M, int64_t N, int64_t K, int split, size_t ws_bytes) {
+  Plan dp;
+  dp.kidx = auto_kernel(layout, dtype, M, N, K);
+  if (split < 0 || ws_bytes == 0) return dp;
+  const Plan sk = split_plan(layout, dtype, M, N, K, split);
+  if (sk.split == 0 || sk.ws_bytes > ws_bytes) return dp;
+  if (split > 0) return sk;
+  const int64_t KT = (K + 63) / 64;
+  double best = dp_cost(0, M, N, KT);
+  for (int i = 1; i < 3; ++i) best = std::min(best, dp_cost(i, M, N, KT));
+  return sk.cost < best ? sk : dp;
 }
 
 struct Call {
@@ -138,6 +217,8 @@ struct Call {
   const void *A, *B;
   void *C;
   int64_t lda, ldb, ldc;
+  void *ws = nullptr;  // workspace for a K split (none: no split)
+  size_t ws_bytes = 0;
 };
 
 hgemm_status_t validate(const Call &c) {
@@ -162,24 +243,53 @@ hgemm_status_t validate(const Call &c) {
   return HGEMM_OK;
 }
 
+hgemm_status_t launch(kernel_fn fn, int64_t grid, const GemmArgs &a, void *stream) {
+  // hipGetLastError() reports the last error of any earlier runtime call on
+  // this thread too: clear it so that only the launch's own result is seen
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return HGEMM_ERR_HIP;
+  }
+  return HGEMM_OK;
+}
+
 hgemm_status_t run(const Call &c, void *stream, const hgemm_config_t *cfg) {
   hgemm_status_t st = validate(c);
   if (st != HGEMM_OK) return st;
-  int kidx = -1, group_m = 0, xcd = 1;
+  int kidx = -1, group_m = 0, xcd = 1, split = 0;
   if (cfg != nullptr) {
-    if (cfg->reserved != 0 || cfg->group_m < 0 || cfg->xcd_remap < -1 || cfg->xcd_remap > 1 ||
-        cfg->kernel < -1 || cfg->kernel >= kTableSize)
+    if (cfg->split < -1 || cfg->split == 1 || cfg->group_m < 0 || cfg->xcd_remap < -1 ||
+        cfg->xcd_remap > 1 || cfg->kernel < -1 || cfg->kernel >= kTableSize)
       return HGEMM_ERR_INVALID_ARG;
     kidx = cfg->kernel;
     group_m = cfg->group_m;
     if (cfg->xcd_remap >= 0) xcd = cfg->xcd_remap;
+    split = cfg->split;
   }
+  if (split > 0 && c.ws == nullptr) return HGEMM_ERR_INVALID_ARG;  // a split needs a workspace
+  if (c.ws != nullptr && (reinterpret_cast<uintptr_t>(c.ws) & 15) != 0)
+    return HGEMM_ERR_UNSUPPORTED;
   if (kidx >= 0 && (kTable[kidx].layout != c.layout || kTable[kidx].dtype != c.dtype))
     return HGEMM_ERR_INVALID_ARG;
   if (c.M == 0 || c.N == 0) return HGEMM_OK;
-  if (kidx < 0) kidx = auto_kernel(c.layout, c.dtype, c.M, c.N);
-  if (kidx < 0) return HGEMM_ERR_UNSUPPORTED;
-  const KernelEntry &e = kTable[kidx];
+  Plan plan;
+  if (kidx < 0) {
+    plan = choose(c.layout, c.dtype, c.M, c.N, c.K, split, c.ws != nullptr ? c.ws_bytes : 0);
+  } else {
+    plan.kidx = kidx;
+    if (split > 0) {
+      if (kTable[kidx].bm != 256 || !kTable[kidx].general) return HGEMM_ERR_UNSUPPORTED;
+      plan = split_plan(c.layout, c.dtype, c.M, c.N, c.K, split);
+      plan.kidx = kidx;
+    }
+  }
+  if (split > 0 && (plan.split == 0 || plan.ws_bytes > c.ws_bytes))
+    return HGEMM_ERR_UNSUPPORTED;  // no tail to split, or the workspace is too small
+  if (plan.kidx < 0) return HGEMM_ERR_UNSUPPORTED;
+  const KernelEntry &e = kTable[plan.kidx];
   if (!e.general) {
     const bool packed = c.lda == c.K && c.ldb == (b_mn_major(c.layout) ? c.N : c.K) &&
                         c.ldc == c.N;
@@ -203,16 +313,27 @@ hgemm_status_t run(const Call &c, void *stream, const hgemm_config_t *cfg) {
   a.beta = c.beta;
   a.group_m = group_m;
   a.xcd_remap = xcd;
-  // hipGetLastError() reports the last error of any earlier runtime call on
-  // this thread too: clear it so that only the launch's own result is seen
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(e.fn, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) {
-    g_last_hip_error = (int)err;
-    return HGEMM_ERR_HIP;
+  a.tile_begin = 0;
+  a.grid = (int)tiles;
+  a.sk_split = 0;
+  a.sk_tiles = 0;
+  a.ws = nullptr;
+  if (plan.split == 0) return launch(e.fn, tiles, a, stream);
+  // whole rounds without a split, then the tail: its K segments, then the sums
+  if (plan.dp_tiles > 0) {
+    a.grid = (int)plan.dp_tiles;
+    st = launch(e.fn, plan.dp_tiles, a, stream);
+    if (st != HGEMM_OK) return st;
   }
-  return HGEMM_OK;
+  a.tile_begin = (int)plan.dp_tiles;
+  a.sk_split = plan.split;
+  a.sk_tiles = (int)plan.sk_tiles;
+  a.ws = static_cast<float *>(c.ws);
+  a.grid = (int)(plan.sk_tiles * plan.split);
+  st = launch(e.split_fn, a.grid, a, stream);
+  if (st != HGEMM_OK) return st;
+  a.grid = (int)plan.sk_tiles * fixup_parts(e.bm, e.bn);
+  return launch(e.fixup, a.grid, a, stream);
 }
 
 // The pages' two layouts: packed storage, alpha 1, beta 0.
@@ -269,6 +390,33 @@ hgemm_status_t hgemm_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, int
                        nullptr);
 }
 
+size_t hgemm_gemm_ws_size(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype) {
+  const int layout = layout_of(opA, opB);
+  if (layout < 0 || M <= 0 || N <= 0 || K <= 0 || (dtype != HGEMM_F16 && dtype != HGEMM_BF16))
+    return 0;
+  return choose(layout, dtype, M, N, K, 0, SIZE_MAX).ws_bytes;
+}
+
+hgemm_status_t hgemm_gemm_ws_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
+                                float alpha, const void *A, int64_t lda, const void *B,
+                                int64_t ldb, float beta, void *C, int64_t ldc, void *workspace,
+                                size_t ws_bytes, void *stream, const hgemm_config_t *cfg) {
+  const int layout = layout_of(opA, opB);
+  if (layout < 0) return HGEMM_ERR_INVALID_ARG;
+  Call c{layout, M, N, K, dtype, alpha, beta, A, B, C, lda, ldb, ldc};
+  c.ws = workspace;
+  c.ws_bytes = workspace != nullptr ? ws_bytes : 0;
+  return run(c, stream, cfg);
+}
+
+hgemm_status_t hgemm_gemm_ws(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
+                             float alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
+                             float beta, void *C, int64_t ldc, void *workspace, size_t ws_bytes,
+                             void *stream) {
+  return hgemm_gemm_ws_ex(opA, opB, M, N, K, dtype, alpha, A, lda, B, ldb, beta, C, ldc,
+                          workspace, ws_bytes, stream, nullptr);
+}
+
 const char *hgemm_status_string(int status) {
   switch (status) {
     case HGEMM_OK: return "ok";
@@ -281,7 +429,7 @@ const char *hgemm_status_string(int status) {
 
 int hgemm_last_hip_error(void) { return g_last_hip_error; }
 
-const char *hgemm_version(void) { return "hgemm-gfx950 1.1"; }
+const char *hgemm_version(void) { return "hgemm-gfx950 1.2"; }
 
 int hgemm_kernel_count(void) { return kTableSize; }
 
@@ -301,7 +449,7 @@ int hgemm_auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K) {
   if (layout < kTN || layout > kAtNN || (dtype != HGEMM_F16 && dtype != HGEMM_BF16) || M <= 0 ||
       N <= 0)
     return -1;
-  return auto_kernel(layout, dtype, M, N);
+  return auto_kernel(layout, dtype, M, N, K);
 }
 
 }  // extern "C"

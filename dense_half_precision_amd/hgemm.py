@@ -34,7 +34,7 @@ class HgemmError(RuntimeError):
 
 class Config(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("group_m", ctypes.c_int32),
-                ("xcd_remap", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("xcd_remap", ctypes.c_int32), ("split", ctypes.c_int32)]
 
 
 _LIB = None
@@ -70,6 +70,13 @@ def _lib() -> ctypes.CDLL:
     lib.hgemm_gemm.restype = i32
     lib.hgemm_gemm_ex.argtypes = general + [ctypes.POINTER(Config)]
     lib.hgemm_gemm_ex.restype = i32
+    ws = general[:-1] + [vp, ctypes.c_size_t, vp]
+    lib.hgemm_gemm_ws.argtypes = ws
+    lib.hgemm_gemm_ws.restype = i32
+    lib.hgemm_gemm_ws_ex.argtypes = ws + [ctypes.POINTER(Config)]
+    lib.hgemm_gemm_ws_ex.restype = i32
+    lib.hgemm_gemm_ws_size.argtypes = [i32, i32, i64, i64, i64, i32]
+    lib.hgemm_gemm_ws_size.restype = ctypes.c_size_t
     lib.hgemm_status_string.argtypes = [i32]
     lib.hgemm_status_string.restype = ctypes.c_char_p
     lib.hgemm_last_hip_error.restype = i32
@@ -159,6 +166,22 @@ def hgemm_gemm(opA, opB, M, N, K, dtype, alpha, A, lda, B, ldb, beta, C, ldc, st
     return _lib().hgemm_gemm_ex(*args, ctypes.byref(cfg))
 
 
+def hgemm_gemm_ws(opA, opB, M, N, K, dtype, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                  ws_bytes, stream=0, kernel=None, group_m=0, xcd_remap=-1, split=0) -> int:
+    """General form with a workspace for the K split of the tail (see
+    include/hgemm.h); with any option set, hgemm_gemm_ws_ex."""
+    args = (opA, opB, M, N, K, _dt(dtype), float(alpha), A, lda, B, ldb, float(beta), C, ldc,
+            workspace, ws_bytes, stream)
+    if kernel is None and group_m == 0 and xcd_remap == -1 and split == 0:
+        return _lib().hgemm_gemm_ws(*args)
+    cfg = Config(-1 if kernel is None else kernel, group_m, xcd_remap, split)
+    return _lib().hgemm_gemm_ws_ex(*args, ctypes.byref(cfg))
+
+
+def gemm_ws_size(opA, opB, M, N, K, dtype) -> int:
+    return _lib().hgemm_gemm_ws_size(opA, opB, M, N, K, _dt(dtype))
+
+
 def kernel_table() -> list[dict]:
     out = []
     for i in range(_lib().hgemm_kernel_count()):
@@ -246,13 +269,15 @@ def matmul_nn(A, B, out=None, stream=None, **cfg):
     return out
 
 
-def gemm(A, B, C=None, alpha=1.0, beta=0.0, transA=False, transB=False, stream=None, **cfg):
+def gemm(A, B, C=None, alpha=1.0, beta=0.0, transA=False, transB=False, stream=None,
+         workspace=None, **cfg):
     """C = alpha * op(A) @ op(B) + beta * C for 2-D CUDA tensors of one dtype.
 
     op(X) is X, or X.T when the trans flag is set (the tensor then holds the
     operand stored transposed).  Rows may be strided (leading dimension =
     stride(0)); columns must be contiguous.  With beta == 0, C (if given) is
-    only written.
+    only written.  `workspace` (a contiguous CUDA tensor, gemm_ws_size bytes
+    or more) allows the K split of the tail tiles.
     """
     import torch
     for name, t in (("A", A), ("B", B)):
@@ -270,10 +295,18 @@ def gemm(A, B, C=None, alpha=1.0, beta=0.0, transA=False, transB=False, stream=N
         C = torch.empty((M, N), dtype=A.dtype, device=A.device)
     elif C.shape != (M, N) or C.dtype != A.dtype or C.stride(1) != 1:
         raise ValueError("C must be [M, N] of the input dtype with contiguous rows")
-    st = hgemm_gemm(OP_T if transA else OP_N, OP_T if transB else OP_N, M, N, K,
-                    _torch_dtype_code(A), alpha, A.data_ptr(), A.stride(0), B.data_ptr(),
-                    B.stride(0), beta, C.data_ptr(), C.stride(0), _stream_ptr(stream), **cfg)
-    _check(st, "hgemm_gemm")
+    opA, opB = OP_T if transA else OP_N, OP_T if transB else OP_N
+    args = (opA, opB, M, N, K, _torch_dtype_code(A), alpha, A.data_ptr(), A.stride(0),
+            B.data_ptr(), B.stride(0), beta, C.data_ptr(), C.stride(0))
+    if workspace is None:
+        st = hgemm_gemm(*args, _stream_ptr(stream), **cfg)
+        _check(st, "hgemm_gemm")
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous CUDA tensor")
+        nbytes = workspace.numel() * workspace.element_size()
+        st = hgemm_gemm_ws(*args, workspace.data_ptr(), nbytes, _stream_ptr(stream), **cfg)
+        _check(st, "hgemm_gemm_ws")
     return C
 
 

@@ -44,6 +44,7 @@
 #ifndef HGEMM_H
 #define HGEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -134,7 +135,10 @@ typedef struct hgemm_config {
                         (>= 1), or 0 for the kernel's default */
   int32_t xcd_remap; /* 1: give each XCD a contiguous range of tiles;
                         0: plain dispatch order; -1: default (on) */
-  int32_t reserved;  /* must be 0 */
+  int32_t split;     /* K split of the tail (see hgemm_gemm_ws): 0 = automatic
+                        (no split without a workspace), -1 = none, S >= 2 =
+                        S segments per tail tile (needs a workspace and a
+                        256 x 256 kernel) */
 } hgemm_config_t;
 
 /* As hgemm_tn / hgemm_nn, with an explicit configuration (NULL = automatic). */
@@ -144,6 +148,47 @@ hgemm_status_t hgemm_tn_ex(int64_t M, int64_t N, int64_t K, int dtype,
 hgemm_status_t hgemm_nn_ex(int64_t M, int64_t N, int64_t K, int dtype,
                            const void *A, const void *B, void *C, void *stream,
                            const hgemm_config_t *cfg);
+/*
+ * General form with a workspace, for shapes whose tiles leave the last round
+ * of workgroups under-filled (the idle units of the MTT S4000 post, section
+ * 3.9.2, and the persistent-kernel section of the tcgen05 translation; here a
+ * K split rather than a persistent kernel): when the tiles of the 256 x 256
+ * kernel do not fill whole rounds of the 256 CUs, the tiles of the last,
+ * partial round (the tail) are each cut into S K segments that run side by
+ * side; each segment writes its FP32 partial sums (256 KiB) to the
+ * workspace, and a second kernel adds the S segments of a tile in segment
+ * order and writes C with alpha, beta and one rounding.
+ * The result is deterministic; it differs from the unsplit one only in the
+ * FP32 summation order.  Up to three launches are enqueued on `stream` (the
+ * whole rounds, the segments, the sums); the workspace must stay untouched
+ * until they complete, and calls that overlap in time must not share one.
+ * Status codes as for hgemm_gemm, plus HGEMM_ERR_UNSUPPORTED for a workspace
+ * that is not 16-byte aligned.
+ *
+ * With cfg->split == 0 (automatic; hgemm_gemm_ws) the library splits only
+ * when its cost estimate says the split is faster than every unsplit tile
+ * size, choosing S by the same estimate.
+ * hgemm_gemm_ws_size returns the workspace bytes the automatic choice would
+ * use for this call (0 when it would not split; 0 for an invalid operation
+ * flag, dtype or dimension <= 0).  With a workspace smaller than that (or
+ * NULL) the call runs unsplit.
+ * workspace: device memory, 16-byte aligned, owned by the caller.
+ */
+size_t hgemm_gemm_ws_size(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype);
+
+hgemm_status_t hgemm_gemm_ws(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
+                             float alpha, const void *A, int64_t lda, const void *B,
+                             int64_t ldb, float beta, void *C, int64_t ldc, void *workspace,
+                             size_t ws_bytes, void *stream);
+
+/* As hgemm_gemm_ws, with an explicit configuration (NULL = automatic);
+ * cfg->split > 0 forces that split (HGEMM_ERR_UNSUPPORTED when there is no
+ * tail, S exceeds the K steps, or the workspace is too small). */
+hgemm_status_t hgemm_gemm_ws_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
+                                float alpha, const void *A, int64_t lda, const void *B,
+                                int64_t ldb, float beta, void *C, int64_t ldc, void *workspace,
+                                size_t ws_bytes, void *stream, const hgemm_config_t *cfg);
+
 /* As hgemm_gemm, with an explicit configuration (NULL = automatic). */
 hgemm_status_t hgemm_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K,
                              int dtype, float alpha, const void *A, int64_t lda,

@@ -140,3 +140,28 @@ def gpu_gemm_general(opA: int, opB: int, dtype: str, M: int, N: int, K: int, A_s
     assert st == hgemm.OK, (f"gemm op{opA}{opB} {dtype} {M}x{N}x{K}: status {st}, hipError_t "
                             f"{hgemm.lib().hgemm_last_hip_error()}")
     return to_host(dC)
+
+
+def gpu_gemm_ws(opA: int, opB: int, dtype: str, M: int, N: int, K: int, A_st: np.ndarray,
+                B_st: np.ndarray, alpha: float = 1.0, beta: float = 0.0,
+                C_st: np.ndarray | None = None, ws_bytes: int | None = None, split: int = 0,
+                kernel: int | None = None) -> np.ndarray:
+    """hgemm_gemm_ws through the C ABI (a K split of the tail with a workspace
+    of ws_bytes, by default the size hgemm_gemm_ws_size reports, at least
+    16 bytes); the workspace is filled with NaN first, so that a partial sum
+    read before it was written shows.  Returns the whole stored C."""
+    import torch
+    from dense_half_precision_amd import hgemm
+    if C_st is None:
+        C_st = np.full((M, N + 8), 0x7E00 if dtype == "f16" else 0x7FC0, dtype=np.uint16)
+    if ws_bytes is None:
+        ws_bytes = hgemm.gemm_ws_size(opA, opB, M, N, K, dtype)
+    ws = torch.full((max(ws_bytes + 3, 16) // 4,), float("nan"), dtype=torch.float32,
+                    device="cuda")
+    dA, dB, dC = to_dev(A_st), to_dev(B_st), to_dev(C_st)
+    st = hgemm.hgemm_gemm_ws(opA, opB, M, N, K, dtype, alpha, dA.data_ptr(), A_st.shape[1],
+                             dB.data_ptr(), B_st.shape[1], beta, dC.data_ptr(), C_st.shape[1],
+                             ws.data_ptr(), ws_bytes, stream_ptr(), kernel=kernel, split=split)
+    assert st == hgemm.OK, (f"gemm_ws op{opA}{opB} {dtype} {M}x{N}x{K} split {split}: status "
+                            f"{st}, hipError_t {hgemm.lib().hgemm_last_hip_error()}")
+    return to_host(dC)

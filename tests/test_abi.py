@@ -97,9 +97,48 @@ def test_ex_config_validation():
     assert hgemm.hgemm_tn_ex(8, 8, 8, 0, FAKE, FAKE, FAKE, kernel=len(tab)) == inv
     assert hgemm.hgemm_tn_ex(8, 8, 8, 0, FAKE, FAKE, FAKE, group_m=-1) == inv
     assert hgemm.hgemm_tn_ex(8, 8, 8, 0, FAKE, FAKE, FAKE, xcd_remap=2) == inv
-    cfg = hgemm.Config(-1, 0, -1, 5)  # reserved must be 0
+    cfg = hgemm.Config(-1, 0, -1, 5)  # a K split needs a workspace
     st = hgemm.lib().hgemm_tn_ex(8, 8, 8, 0, FAKE, FAKE, FAKE, 0, ctypes.byref(cfg))
     assert st == inv
+
+
+def test_split_workspace_size_and_validation():
+    """The workspace the automatic K split asks for, and the refusals of a
+    forced split, all decided on the host before any launch."""
+    inv, uns = hgemm.ERR_INVALID_ARG, hgemm.ERR_UNSUPPORTED
+    size = hgemm.gemm_ws_size
+    # 6144^2: 24 x 24 = 576 tiles of 256 x 256 = 2 rounds of 256 CUs + a tail
+    # of 64 tiles; the estimate is least at 4 segments (one wave of 256), 256
+    # KiB of partial sums each
+    assert size(0, 1, 6144, 6144, 6144, "f16") == 64 * 4 * 256 * 256 * 4
+    assert size(0, 0, 6144, 6144, 6144, "bf16") == 64 * 4 * 256 * 256 * 4
+    assert size(0, 1, 8192, 8192, 8192, "f16") == 0      # 1024 tiles: whole rounds
+    assert size(0, 1, 2048, 2048, 64, "f16") == 0        # one K step: nothing to split
+    # 512 x 512 x 65536: 4 tiles, 1024 K steps: 64 segments each fill the CUs
+    assert size(0, 1, 512, 512, 65536, "f16") == 4 * 64 * 256 * 256 * 4
+    # 4352 x 4352 x 1024: a tail of 33 tiles of 16 steps; the 128 x 128 tile
+    # without a split is estimated faster
+    assert size(0, 1, 4352, 4352, 1024, "f16") == 0
+    assert size(2, 1, 6144, 6144, 6144, "f16") == 0      # bad operation flag
+    assert size(0, 1, 0, 6144, 6144, "f16") == 0
+    assert size(0, 1, 6144, 6144, 6144, 5) == 0
+
+    g = hgemm.hgemm_gemm_ws
+    M = N = K = 6144
+    need = size(0, 1, M, N, K, "f16")
+
+    def call(split, ws=FAKE, nbytes=need, kernel=None, m=M, n=N, k=K):
+        return g(0, 1, m, n, k, "f16", 1.0, FAKE, k, FAKE, k, 0.0, FAKE, n, ws, nbytes,
+                 kernel=kernel, split=split)
+    assert call(1) == inv                       # one segment is no split
+    assert call(-2) == inv
+    assert call(4, ws=0, nbytes=0) == inv       # a forced split needs a workspace
+    assert call(4, ws=FAKE + 8) == uns          # workspace not 16-byte aligned
+    assert call(4, nbytes=need - 1) == uns      # too small for the forced split
+    assert call(97, nbytes=1 << 40) == uns      # more segments than the 96 K steps
+    assert call(4, m=8192, n=8192, k=8192) == uns  # no tail to split
+    k128 = hgemm.kernel_index("tn_f16_128x128x64")
+    assert call(4, kernel=k128) == uns          # the split runs the 256 x 256 kernels only
 
 
 def test_kernel_table_and_auto_choice():
