@@ -170,11 +170,13 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T:
     epilogue(std::true_type{});
 }
 
-// SPLIT: the workgroup computes one K segment of a tile and writes FP32
-// partial sums to the workspace (a separate instantiation, so that the
-// data-parallel kernel carries none of the segment bookkeeping in registers).
+// One tile (position `tile` of the grouped tile order) by one workgroup.
+// SPLIT: only K segment `seg` of sk_split, whose FP32 partial sums go to
+// workspace slot `slot` (a separate instantiation, so that whole-K tiles
+// carry none of the segment bookkeeping in registers).
 template <class T, int LAYOUT, int DT, bool SPLIT>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int tile, int seg,
+                                          int slot) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
   constexpr int FM = T::FM, FN = T::FN, NMF = T::NMF;
   constexpr int SEG_A = T::SEG_A, SEG_B = T::SEG_B;
@@ -190,30 +192,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   // is no tracked read, and an explicit wait opens each slice instead.
   constexpr bool A_FIRST = A_MN && !B_MN;
   constexpr bool ALL_TR = A_MN && B_MN;
-  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
 
-  const int M = args.M, N = args.N, K = args.K;
+  const int M = args.M, N = args.N;
   const int lda = args.lda, ldb = args.ldb;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  // This workgroup's tile and K steps: position `pos` of the launch; with a K
-  // split, tile pos % sk_tiles of the launch's range, segment pos / sk_tiles,
-  // steps [seg*KT/S, (seg+1)*KT/S).
-  const int KT_all = (K + BK - 1) / BK;
-  const int pos = __builtin_amdgcn_readfirstlane(xcd_position(blockIdx.x, args.grid, args.xcd_remap));
+  // K range of this workgroup: all of it, or steps [seg*KT/S, (seg+1)*KT/S)
+  // of a split.  A segment is computed as a GEMM of its own: the operand
+  // panels start at its first k and K is its length, so that the main loop
+  // below is the same code either way.
+  const int KT_all = (args.K + BK - 1) / BK;
   const int S = SPLIT ? args.sk_split : 1;
-  const int seg = SPLIT ? pos / args.sk_tiles : 0;
+  const int k_begin = SPLIT ? __builtin_amdgcn_readfirstlane(seg * KT_all / S) * BK : 0;
+  const int K = SPLIT ? __builtin_amdgcn_readfirstlane(
+                            min(args.K, (seg + 1) * KT_all / S * BK) - k_begin)
+                      : args.K;
   int tm, tn;
-  tile_of(args.tile_begin + (SPLIT ? pos % args.sk_tiles : pos), tiles_m, tiles_n, args.group_m,
-          tm, tn);
+  tile_of(tile, tiles_m, tiles_n, args.group_m, tm, tn);
   // the tile order divides on the vector unit; the results are uniform and are
   // moved to scalar registers explicitly, so that the buffer descriptors built
   // from them stay scalar (a descriptor held in vector registers turns every
   // load into a per-lane loop)
   const int m0 = __builtin_amdgcn_readfirstlane(tm * BM);
   const int n0 = __builtin_amdgcn_readfirstlane(tn * BN);
-  const int s_begin = SPLIT ? __builtin_amdgcn_readfirstlane(seg * KT_all / S) : 0;
-  const int s_end = SPLIT ? __builtin_amdgcn_readfirstlane((seg + 1) * KT_all / S) : KT_all;
-  const int K_end = SPLIT ? min(K, s_end * BK) : K;  // K limit of this workgroup's loads
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -228,11 +228,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   // m/n-chunk (lane%CPR) ^ nn_chunk_xor(k); chunks past the M/N edge (a
   // multiple of 8) read out of range.
   // Wave w loads segments w*SEG .. w*SEG+SEG-1 of each operand.
-  auto kmaj_off = [&](int seg, int ld, int &chunk) {
-    return kmajor_load_offset<T::LDS>(seg, lane, ld, chunk);
+  auto kmaj_off = [&](int part, int ld, int &chunk) {
+    return kmajor_load_offset<T::LDS>(part, lane, ld, chunk);
   };
-  auto mnmaj_off = [&](int seg, int ld, int rowb, int x0, int xdim, int &chunk) {
-    return mnmajor_load_offset<T::LDS>(seg, lane, ld, rowb, x0, xdim, chunk);
+  auto mnmaj_off = [&](int part, int ld, int rowb, int x0, int xdim, int &chunk) {
+    return mnmajor_load_offset<T::LDS>(part, lane, ld, rowb, x0, xdim, chunk);
   };
   uint32_t a_off[SEG_A];
   int a_chunk[SEG_A];
@@ -246,8 +246,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   for (int i = 0; i < SEG_B; ++i)
     b_off[i] = B_MN ? mnmaj_off(wave * SEG_B + i, ldb, 2 * BN, n0, N, b_chunk[i])
                     : kmaj_off(wave * SEG_B + i, ldb, b_chunk[i]);
-  const uint16_t *a_panel = A_MN ? args.A + m0 : args.A + (size_t)m0 * lda;
-  const uint16_t *b_panel = B_MN ? args.B + n0 : args.B + (size_t)n0 * ldb;
+  const uint16_t *a_panel =
+      A_MN ? args.A + m0 + (size_t)k_begin * lda : args.A + (size_t)m0 * lda + k_begin;
+  const uint16_t *b_panel =
+      B_MN ? args.B + n0 + (size_t)k_begin * ldb : args.B + (size_t)n0 * ldb + k_begin;
 
   // A stage of step s at (s % 3) * A_STAGE, B stage at B_BASE + (s & 1) * B_STAGE
   auto a_base = [&](int s) { return (uint32_t)((s % 3) * T::A_STAGE); };
@@ -260,11 +262,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   // (One descriptor built from selected base and size: descriptors merged from
   // branches lose their uniformity and end up in a per-lane loop.)
   auto rsrc_of = [&](bool mn, const uint16_t *panel, int ld, int rows, int k0) {
-    const int krem = K_end - k0;
+    const int krem = K - k0;
     const uint16_t *base = mn ? panel + (size_t)k0 * ld : panel + k0;
     const uint32_t bytes = krem <= 0 ? 0u
                            : mn      ? (uint32_t)(min(krem, BK) * ld) * 2u
-                                     : (uint32_t)((rows - 1) * ld + K_end - k0) * 2u;
+                                     : (uint32_t)((rows - 1) * ld + K - k0) * 2u;
     return make_rsrc(base, bytes);
   };
   __amdgpu_buffer_rsrc_t rs_a, rs_b;
@@ -374,25 +376,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
-  // steps are counted from s_begin (stage ring positions) and loaded at
-  // absolute k = (s_begin + step) * BK; `tail` is an absolute step index
-  const int KT = s_end - s_begin;
+  const int KT = (K + BK - 1) / BK;
 
   // ---- prologue: A of steps 0, 1 and B of step 0 in flight; slice 0 read ----
-  if (tail == s_begin) mask_tail();
-  prep_a(s_begin);
+  if (tail == 0) mask_tail();
+  prep_a(0);
 #pragma unroll
   for (int i = 0; i < SEG_A; ++i) load_a(a_base(0), i);
-  prep_b(s_begin);
+  prep_b(0);
 #pragma unroll
   for (int i = 0; i < SEG_B; ++i) load_b(b_base(0), i);
-  if (tail == s_begin + 1) mask_tail();
-  prep_a(s_begin + 1);
+  if (tail == 1) mask_tail();
+  prep_a(1);
 #pragma unroll
   for (int i = 0; i < SEG_A; ++i) load_a(a_base(1), i);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(SEG_A, 0));
   wg_barrier();
-  prep_b(s_begin + 1);
+  prep_b(1);
 #pragma unroll
   for (int q = 0; q < NR; ++q) {
     read_op(I0{}, a_base(0), b_base(0), 0, q);
@@ -402,11 +402,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
 
   // ---- main loop -------------------------------------------------------------
   for (int kt = 0; kt < KT; ++kt) {
-    if (s_begin + kt + 2 == tail) mask_tail();  // loads of steps kt+2 on are issued below
+    if (kt + 2 == tail) mask_tail();  // loads of steps kt+2 on are issued below
     const uint32_t ca = a_base(kt), cb = b_base(kt);
     const uint32_t na = a_base(kt + 1), nb = b_base(kt + 1);
     // X: slice 0; read slice 1; A of step kt+2 into the stage step kt-1 used
-    prep_a(s_begin + kt + 2);
+    prep_a(kt + 2);
     const uint32_t la = a_base(kt + 2);
     wait_set(I0{});
 #pragma unroll
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(SEG_A, 0));
     wg_barrier();
     // Z: second half of slice 1; read slice 0 of step kt+1; B of step kt+2
-    prep_b(s_begin + kt + 2);
+    prep_b(kt + 2);
     const uint32_t lb = b_base(kt + 2);
 #pragma unroll
     for (int t = NMF / 2; t < NMF; ++t) {
@@ -464,16 +464,59 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
     // a K segment: its FP32 sums go to workspace slot `pos`, each wave's block
     // in lane order (16-byte stores, 1 KiB per instruction); the fixup kernel
     // adds the segments of the tile in order and writes C
-    float *slot = args.ws + ((size_t)pos * 4 + wave) * (FM * FN * 256);
+    // (stored straight from the accumulator registers: a plain store made the
+    // compiler shuttle accumulators between register files inside the loop.
+    // The compiler does not pad inline assembly for the matrix-core result
+    // latency, so 24 wait states first: more than the 19 the slowest MFMA
+    // needs before a memory instruction may read its result.)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    float *dst = args.ws + ((size_t)slot * 4 + wave) * (FM * FN * 256) + lane * 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) *(f32x4 *)(slot + ((i * FN + j) * 64 + lane) * 4) = acc[i][j];
+      for (int j = 0; j < FN; ++j)
+        asm volatile("global_store_dwordx4 %0, %1, off"
+                     :
+                     : "v"(dst + (i * FN + j) * 256), "a"(acc[i][j])
+                     : "memory");
   } else {
     store_tile<T, DT>(args, acc, smem, m0, n0, wave, lane);
   }
 }
 
+// Launch modes (the position of a workgroup is its index after the XCD remap
+// of its part of the grid):
+//   kWhole: `grid` whole-K tiles, positions tile_begin + p;
+//   kSegments: sk_tiles * sk_split K segments, position p = segment
+//     p / sk_tiles of tile tile_begin + p % sk_tiles, written to slot p;
+//   kMixed: `grid` whole-K tiles 0 .. grid-1 (whole rounds: a multiple of
+//     the 8 XCDs, so the segments after them keep the XCD placement the
+//     remap assumes), then the segments of kSegments, in one launch: the
+//     short segments fill the CUs as the last whole tiles finish, with no
+//     launch boundary between them, and their partial sums are written last,
+//     while the caches still hold them for the fixup.
+enum LaunchMode { kWhole = 0, kSegments = 1, kMixed = 2 };
+
+template <class T, int LAYOUT, int DT, int MODE>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+  const int b = blockIdx.x;
+  if constexpr (MODE == kWhole) {
+    const int p = __builtin_amdgcn_readfirstlane(xcd_position(b, args.grid, args.xcd_remap));
+    gemm_tile<T, LAYOUT, DT, false>(args, smem, args.tile_begin + p, 0, 0);
+  } else {
+    const int dp = MODE == kMixed ? args.grid : 0;  // whole tiles ahead of the segments
+    if (MODE == kMixed && b < dp) {
+      const int p = __builtin_amdgcn_readfirstlane(xcd_position(b, dp, args.xcd_remap));
+      gemm_tile<T, LAYOUT, DT, false>(args, smem, p, 0, 0);
+    } else {
+      const int nseg = args.sk_tiles * args.sk_split;
+      const int p = __builtin_amdgcn_readfirstlane(xcd_position(b - dp, nseg, args.xcd_remap));
+      gemm_tile<T, LAYOUT, DT, true>(args, smem, args.tile_begin + p % args.sk_tiles,
+                                     p / args.sk_tiles, p);
+    }
+  }
+}
 
 // Second half of a K-split launch: the S FP32 partial sums of each split tile
 // are added in segment order (so the result does not depend on which segment

@@ -26,21 +26,22 @@ struct KernelEntry {
   bool production;  // candidate of the automatic choice
   bool general;     // honours leading dimensions, alpha, beta and K splits
   kernel_fn fn;
-  kernel_fn split_fn;  // one K segment of a tile into the workspace (general kernels)
+  kernel_fn split_fn;  // K segments of the tail tiles only (general kernels)
+  kernel_fn mixed_fn;  // K segments, then whole tiles, in one launch (general kernels)
   kernel_fn fixup;     // adds the K segments of split tiles (general kernels)
 };
 
 template <class T, int LAYOUT, int DT>
 constexpr KernelEntry entry(const char *name, int group_m, bool production) {
   return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, production, true,
-                     &gemm_kernel<T, LAYOUT, DT, false>, &gemm_kernel<T, LAYOUT, DT, true>,
-                     &gemm_sk_fixup<T, DT>};
+                     &gemm_kernel<T, LAYOUT, DT, kWhole>, &gemm_kernel<T, LAYOUT, DT, kSegments>,
+                     &gemm_kernel<T, LAYOUT, DT, kMixed>, &gemm_sk_fixup<T, DT>};
 }
 // the register-staged baseline assumes packed TN/NN operands, alpha 1, beta 0
 template <class T, int LAYOUT, int DT>
 constexpr KernelEntry rs_entry(const char *name, int group_m) {
   return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, false, false,
-                     &regstage_kernel<T, LAYOUT, DT>, nullptr, nullptr};
+                     &regstage_kernel<T, LAYOUT, DT>, nullptr, nullptr, nullptr};
 }
 
 using T256 = TileCfg<256, 256>;
@@ -118,14 +119,14 @@ int find_kernel(int layout, int dtype, int bm) {
 // KT * (t/256)^2 / rate_t units, rate_t the per-CU throughput of that tile size
 // at full occupancy relative to the 256 kernel (128: 0.8, 64: 0.5, measured).
 // Cost model of the automatic choice, in units of one K step of a 256 x 256
-// tile on every CU at once (about 1.3 us on this chip), fitted to measured
-// times of the kernels below over square and skinny shapes.
+// tile on every CU at once (about 1.3 us on this chip); the constants were
+// chosen on measured times of every tile size and split over square, skinny
+// and long-K shapes.
 constexpr int64_t kCUs = 256;
 const int kSizes[3] = {256, 128, 64};
 const double kRate[3] = {1.0, 0.8, 0.5};  // sustained rate relative to the 256 x 256 tile
-constexpr double kTileFixed = 4.0;        // prologue and epilogue of a tile, in K steps
-constexpr double kSplitFixed = 6.9;       // the fixup launch and the wait between launches
-constexpr double kSplitDrain = 5.0;       // the whole-round launch draining before the tail
+constexpr double kTileFixed = 3.0;        // prologue and epilogue of a tile, in K steps
+constexpr double kSplitFixed = 6.9;       // the fixup launch and the wait for it
 constexpr double kSlotCost = 0.055;       // one 256 KiB partial sum written and read back
 constexpr int kMaxAutoSplit = 64;
 constexpr int64_t kMaxSlots = 1024;       // 256 MiB of partial sums at most
@@ -164,7 +165,7 @@ double split_cost(int64_t full_rounds, int64_t tail, int64_t KT, int64_t S) {
   const int64_t waves = (tail * S + kCUs - 1) / kCUs;
   return (double)full_rounds * ((double)KT + kTileFixed) +
          (double)waves * ((double)((KT + S - 1) / S) + kTileFixed) + kSplitFixed +
-         kSlotCost * (double)(tail * S) + (full_rounds > 0 ? kSplitDrain : 0.0);
+         kSlotCost * (double)(tail * S);
 }
 
 // split > 0: that many segments; split == 0: the number with the least
@@ -319,18 +320,20 @@ hgemm_status_t run(const Call &c, void *stream, const hgemm_config_t *cfg) {
   a.sk_tiles = 0;
   a.ws = nullptr;
   if (plan.split == 0) return launch(e.fn, tiles, a, stream);
-  // whole rounds without a split, then the tail: its K segments, then the sums
-  if (plan.dp_tiles > 0) {
-    a.grid = (int)plan.dp_tiles;
-    st = launch(e.fn, plan.dp_tiles, a, stream);
-    if (st != HGEMM_OK) return st;
-  }
+  // the whole rounds' tiles and the tail's K segments in one launch (the
+  // segments alone when there is no whole round), then the sums
   a.tile_begin = (int)plan.dp_tiles;
   a.sk_split = plan.split;
   a.sk_tiles = (int)plan.sk_tiles;
   a.ws = static_cast<float *>(c.ws);
-  a.grid = (int)(plan.sk_tiles * plan.split);
-  st = launch(e.split_fn, a.grid, a, stream);
+  const int64_t nseg = plan.sk_tiles * plan.split;
+  if (plan.dp_tiles > 0) {
+    a.grid = (int)plan.dp_tiles;
+    st = launch(e.mixed_fn, plan.dp_tiles + nseg, a, stream);
+  } else {
+    a.grid = (int)nseg;
+    st = launch(e.split_fn, nseg, a, stream);
+  }
   if (st != HGEMM_OK) return st;
   a.grid = (int)plan.sk_tiles * fixup_parts(e.bm, e.bn);
   return launch(e.fixup, a.grid, a, stream);
