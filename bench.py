@@ -195,6 +195,22 @@ def micro() -> int:
               "b_operand": "pre-transposed (Bt), 16-byte reads" if name.startswith("tn") else
               ("register transpose" if name.startswith("rs") else "transposing LDS read"),
               "ms": round(ms, 4), "tflops": round(w.flops / ms / 1e9, 1)})
+    # wave specialisation (4 loader + 4 MFMA waves, 128 x 256 tile) against the
+    # single-role pipeline on the same tile and the production 256 x 256 kernel
+    for (M, N, K) in ((8192, 8192, 8192), (8192, 8192, 16384)):
+        A = inputs.draw((M, K), "f16", "uniform", 1)
+        Bt = inputs.draw((N, K), "f16", "uniform", 2)
+        dA = torch.from_numpy(A.view(np.int16)).cuda()
+        dB = torch.from_numpy(Bt.view(np.int16)).cuda()
+        dC = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        for name in ("tn_f16_256x256x64", "ws_tn_f16_128x256x64", "tn_f16_128x256x64"):
+            k = hgemm.kernel_index(name)
+            ms = timed(lambda: hgemm.hgemm_tn_ex(M, N, K, "f16", dA.data_ptr(), dB.data_ptr(),
+                                                 dC.data_ptr(), sp, kernel=k), n=50, warm=15)
+            emit({"micro": "wave_specialisation", "shape": f"{M}x{N}x{K}", "kernel": name,
+                  "roles": "4 loader + 4 MFMA waves" if name.startswith("ws_") else "4 waves, both roles",
+                  "ms": round(ms, 4), "tflops": round(2 * M * N * K / ms / 1e9, 1)})
+        del dA, dB, dC
     return 0
 
 
@@ -280,6 +296,8 @@ def main() -> int:
                     help="run the microbenchmarks behind the design choices and exit")
     ap.add_argument("--tail", action="store_true",
                     help="K split of the tail vs the unsplit choice and torch.mm, per shape")
+    ap.add_argument("--vendor", action="store_true",
+                    help="run the workload through torch.mm (the vendor library) instead")
     ap.add_argument("--oracle-table", action="store_true",
                     help="time the CPU oracle on every workload (host only) and exit")
     args = ap.parse_args()
@@ -328,6 +346,24 @@ def main() -> int:
     dC = torch.empty((w.M, w.N), dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
+    if args.vendor:
+        # the same product through torch.mm (the vendor library), for comparison
+        # and for counter runs on it; not a result of this library
+        tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+        a, b = dA.view(tdt), dB.view(tdt)
+        mm = (lambda: torch.mm(a, b.t())) if w.layout == "tn" else (lambda: torch.mm(a, b))
+        for _ in range(args.warmup):
+            mm()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            mm()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / args.steps * 1e3
+        print(json.dumps({"vendor": "torch.mm", "workload": w.name, "steps": args.steps,
+                          "ms_per_step": round(ms, 5), "tflops": round(w.flops / ms / 1e9, 2)}),
+              flush=True)
+        return 0
     fn = hgemm.hgemm_tn_ex if w.layout == "tn" else hgemm.hgemm_nn_ex
     kern = args.kernel if args.kernel >= 0 else hgemm.auto_kernel(
         hgemm.TN if w.layout == "tn" else hgemm.NN, w.dtype, w.M, w.N, w.K)

@@ -11,6 +11,7 @@
 #include "hgemm.h"
 #include "gemm_kernel.hpp"
 #include "gemm_regstage.hpp"
+#include "gemm_ws_kernel.hpp"
 
 namespace {
 
@@ -29,6 +30,7 @@ struct KernelEntry {
   kernel_fn split_fn;  // K segments of the tail tiles only (general kernels)
   kernel_fn mixed_fn;  // K segments, then whole tiles, in one launch (general kernels)
   kernel_fn fixup;     // adds the K segments of split tiles (general kernels)
+  int threads = 256;   // workgroup size
 };
 
 template <class T, int LAYOUT, int DT>
@@ -36,6 +38,13 @@ constexpr KernelEntry entry(const char *name, int group_m, bool production) {
   return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, production, true,
                      &gemm_kernel<T, LAYOUT, DT, kWhole>, &gemm_kernel<T, LAYOUT, DT, kSegments>,
                      &gemm_kernel<T, LAYOUT, DT, kMixed>, &gemm_sk_fixup<T, DT>};
+}
+// producer/consumer wave specialisation: leading dimensions, alpha and beta,
+// no K split; an ablation, never chosen automatically
+template <class T, int DT>
+constexpr KernelEntry ws_entry(const char *name, int group_m) {
+  return KernelEntry{name, kTN, DT, T::BM, T::BN, T::BK, T::LDS, group_m, false, true,
+                     &gemm_ws_kernel<T, DT>, nullptr, nullptr, nullptr, T::NT};
 }
 // the register-staged baseline assumes packed TN/NN operands, alpha 1, beta 0
 template <class T, int LAYOUT, int DT>
@@ -47,6 +56,8 @@ constexpr KernelEntry rs_entry(const char *name, int group_m) {
 using T256 = TileCfg<256, 256>;
 using T128 = TileCfg<128, 128>;
 using T64 = TileCfg<64, 64>;
+using T128x256 = TileCfg<128, 256>;
+using W128x256 = WsCfg<128, 256>;
 using T256Plain = TileCfg<256, 256, kLdsPlain>;
 using T256Direct = TileCfg<256, 256, kLdsXor, 0>;
 using R256 = RsCfg<256, 256, 2, 2, kLdsXor>;
@@ -92,6 +103,12 @@ const KernelEntry kTable[] = {
     entry<T64, kAtTN, kBF16>("at_tn_bf16_64x64x64", 4, true),
     entry<T64, kAtNN, kF16>("at_nn_f16_64x64x64", 4, true),
     entry<T64, kAtNN, kBF16>("at_nn_bf16_64x64x64", 4, true),
+    // wave specialisation: 4 loader + 4 MFMA waves on a 128 x 256 tile, and the
+    // single-role pipeline on the same tile for comparison
+    ws_entry<W128x256, kF16>("ws_tn_f16_128x256x64", 4),
+    ws_entry<W128x256, kBF16>("ws_tn_bf16_128x256x64", 4),
+    entry<T128x256, kTN, kF16>("tn_f16_128x256x64", 4, false),
+    entry<T128x256, kTN, kBF16>("tn_bf16_128x256x64", 4, false),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -244,11 +261,12 @@ hgemm_status_t validate(const Call &c) {
   return HGEMM_OK;
 }
 
-hgemm_status_t launch(kernel_fn fn, int64_t grid, const GemmArgs &a, void *stream) {
+hgemm_status_t launch(kernel_fn fn, int64_t grid, const GemmArgs &a, void *stream,
+                      int threads = 256) {
   // hipGetLastError() reports the last error of any earlier runtime call on
   // this thread too: clear it so that only the launch's own result is seen
   (void)hipGetLastError();
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3((unsigned)threads), 0, (hipStream_t)stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
@@ -282,7 +300,7 @@ hgemm_status_t run(const Call &c, void *stream, const hgemm_config_t *cfg) {
   } else {
     plan.kidx = kidx;
     if (split > 0) {
-      if (kTable[kidx].bm != 256 || !kTable[kidx].general) return HGEMM_ERR_UNSUPPORTED;
+      if (kTable[kidx].bm != 256 || kTable[kidx].split_fn == nullptr) return HGEMM_ERR_UNSUPPORTED;
       plan = split_plan(c.layout, c.dtype, c.M, c.N, c.K, split);
       plan.kidx = kidx;
     }
@@ -319,7 +337,7 @@ hgemm_status_t run(const Call &c, void *stream, const hgemm_config_t *cfg) {
   a.sk_split = 0;
   a.sk_tiles = 0;
   a.ws = nullptr;
-  if (plan.split == 0) return launch(e.fn, tiles, a, stream);
+  if (plan.split == 0) return launch(e.fn, tiles, a, stream, e.threads);
   // the whole rounds' tiles and the tail's K segments in one launch (the
   // segments alone when there is no whole round), then the sums
   a.tile_begin = (int)plan.dp_tiles;

@@ -148,7 +148,7 @@ def test_kernel_table_and_auto_choice():
     for k in tab:
         assert k["layout"] in (0, 1, 2, 3) and k["dtype"] in (0, 1) and k["bk"] == 64
         lay = ("tn", "nn", "at_tn", "at_nn")[k["layout"]]
-        stem = k["name"][3:] if k["name"].startswith("rs_") else k["name"]
+        stem = k["name"][3:] if k["name"][:3] in ("rs_", "ws_") else k["name"]
         assert stem.startswith(f"{lay}_{'f16' if k['dtype'] == 0 else 'bf16'}_")
     # every layout/dtype has an automatic choice, matching layout and dtype
     for lay in (0, 1, 2, 3):
