@@ -401,13 +401,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- main loop -------------------------------------------------------------
+  // stage offsets of steps kt, kt+1, kt+2, rotated at the end of each step
+  // (no division by 3 in the loop)
+  uint32_t ra0 = a_base(0), ra1 = a_base(1), ra2 = a_base(2);
+  uint32_t rb0 = b_base(0), rb1 = b_base(1);
   for (int kt = 0; kt < KT; ++kt) {
     if (kt + 2 == tail) mask_tail();  // loads of steps kt+2 on are issued below
-    const uint32_t ca = a_base(kt), cb = b_base(kt);
-    const uint32_t na = a_base(kt + 1), nb = b_base(kt + 1);
+    const uint32_t ca = ra0, cb = rb0;
+    const uint32_t na = ra1, nb = rb1;
     // X: slice 0; read slice 1; A of step kt+2 into the stage step kt-1 used
     prep_a(kt + 2);
-    const uint32_t la = a_base(kt + 2);
+    const uint32_t la = ra2;
     wait_set(I0{});
 #pragma unroll
     for (int t = 0; t < NMF; ++t) {
@@ -432,7 +436,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
     wg_barrier();
     // Z: second half of slice 1; read slice 0 of step kt+1; B of step kt+2
     prep_b(kt + 2);
-    const uint32_t lb = b_base(kt + 2);
+    const uint32_t lb = rb0;  // step kt+2 reuses the B stage of step kt
 #pragma unroll
     for (int t = NMF / 2; t < NMF; ++t) {
       mfma(I1{}, t);
@@ -446,6 +450,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    const uint32_t r = ra0;
+    ra0 = ra1;
+    ra1 = ra2;
+    ra2 = r;
+    rb0 = rb1;
+    rb1 = cb;
   }
 
   // The last step (or, for K = 0, the prologue) read fragments for a step that
@@ -461,7 +471,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
 
   // ---- epilogue --------------------------------------------------------------
   if constexpr (SPLIT) {
-    // a K segment: its FP32 sums go to workspace slot `pos`, each wave's block
+    // a K segment: its FP32 sums go to workspace slot `slot`, each wave's block
     // in lane order (16-byte stores, 1 KiB per instruction); the fixup kernel
     // adds the segments of the tile in order and writes C
     // (stored straight from the accumulator registers: a plain store made the
