@@ -32,10 +32,16 @@ KERNEL_SOURCES = ["device.hpp", "common.hpp", "gemm_kernel.hpp"]
 
 
 def kernel_source_digest() -> str:
+    """Digest of the benched kernel's device code, comments and layout left out
+    (a comment edit does not change the kernel the counters were taken on)."""
+    import re
     h = hashlib.sha256()
     for s in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "dense_half_precision_amd", "csrc", s), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "dense_half_precision_amd", "csrc", s)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

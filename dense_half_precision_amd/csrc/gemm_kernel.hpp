@@ -42,14 +42,20 @@
 // bare s_barrier with explicit waits: __syncthreads() would wait for every
 // load still in flight.
 //
-// Epilogue: FP32 -> FP16/BF16 (round to nearest even) into a wave-private,
-// padded LDS region, then 16-byte stores of whole 256-byte row segments (the
-// LDS-staged epilogue of the CuTe note and of the S4000 post).
+// Epilogue: C = alpha * sums + beta * C, converted to FP16/BF16 (round to
+// nearest even) into a wave-private, padded LDS region, then 16-byte stores
+// of whole 256-byte row segments (the LDS-staged epilogue of the CuTe note and
+// of the S4000 post).
 //
-// Workgroup order: XCD-aware remap plus grouping by group_m tile rows (see
-// tile_coords), so the tiles resident on one XCD share A and B panels in its
-// L2 (the block swizzle of the HGEMM notes, the grouped order of the tcgen05
-// translation's 2-SM section).
+// Workgroup order: XCD-aware remap plus grouping by group_m tile rows
+// (xcd_position, tile_of), so the tiles resident on one XCD share A and B
+// panels in its L2 (the block swizzle of the HGEMM notes, the grouped order of
+// the tcgen05 translation's 2-SM section).
+//
+// Launch modes (gemm_kernel's last parameter): whole-K tiles; K segments of
+// the tail tiles, whose FP32 partial sums gemm_sk_fixup adds up; or the whole
+// rounds followed by the segments in one launch.  A segment runs the same
+// tile code on a K sub-range.
 #pragma once
 
 #include <type_traits>
