@@ -1,8 +1,10 @@
 // gemm_kernel.hpp -- the HGEMM kernel for gfx950.
 //
-// One workgroup of four 64-wide waves (2 x 2) computes a BM x BN tile of C;
-// each wave owns a (BM/2) x (BN/2) block made of 16x16 MFMA tiles whose FP32
-// accumulators stay in registers for the whole K loop: the output-stationary
+// One workgroup of four 64-wide waves (2 x 2; the wave grid is a parameter,
+// and a 2 x 4 grid of eight waves, two per SIMD, is kept as a measured
+// variant) computes a BM x BN tile of C; each wave owns a block made of 16x16
+// MFMA tiles whose FP32 accumulators stay in registers for the whole K loop
+// (a (BM/2) x (BN/2) block with four waves): the output-stationary
 // tiling of the tcgen05 translation's tiled_matmul recap and the block ->
 // warp -> MMA hierarchy of the HGEMM MMA note (fractal-structure section) and
 // of section 3.1 of the S4000 post.
@@ -64,11 +66,13 @@
 
 namespace hgemm {
 
-template <int BM_, int BN_, int LDS_ = kLdsXor, int EPI_ = 1>
+template <int BM_, int BN_, int LDS_ = kLdsXor, int EPI_ = 1, int WVM_ = 2, int WVN_ = 2>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 64;
-  static constexpr int NT = 256;                      // 4 waves, 2 x 2
-  static constexpr int WTM = BM / 2, WTN = BN / 2;    // wave block
+  static constexpr int WVM = WVM_, WVN = WVN_;        // waves along M and N
+  static constexpr int NW = WVM * WVN;                // waves per workgroup
+  static constexpr int NT = 64 * NW;
+  static constexpr int WTM = BM / WVM, WTN = BN / WVN;  // wave block
   static constexpr int FM = WTM / 16, FN = WTN / 16;  // 16x16 MFMA tiles per wave
   static constexpr int NMF = FM * FN;                 // MFMAs per 32-k slice
   static constexpr int LDS = LDS_;
@@ -78,18 +82,21 @@ struct TileCfg {
   static constexpr int B_BASE = 3 * A_STAGE;          // three A stages, then two B stages
   static constexpr int PIPE_BYTES = 3 * A_STAGE + 2 * B_STAGE;
   static constexpr int CROW = WTN * 2 + 16;           // epilogue row pitch (bytes)
-  static constexpr int EPI_BYTES = EPI ? 4 * WTM * CROW : 0;
+  static constexpr int EPI_BYTES = EPI ? NW * WTM * CROW : 0;
   static constexpr int LDS_BYTES = PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES;
-  static constexpr int SEG_A = BM / 32;               // 1 KiB A segments per wave and step
-  static constexpr int SEG_B = BN / 32;               // 1 KiB B segments per wave and step
+  static constexpr int SEG_A = BM / (8 * NW);         // 1 KiB A segments per wave and step
+  static constexpr int SEG_B = BN / (8 * NW);         // 1 KiB B segments per wave and step
   static_assert(BM % 64 == 0 && BN % 64 == 0 && BM <= 256 && BN <= 256, "tile");
+  static_assert(SEG_A * 8 * NW == BM && SEG_B * 8 * NW == BN, "whole segments per wave");
+  static_assert(WTM % 32 == 0 && WTN % 16 == 0 && (NW == 4 || NW == 8), "wave grid");
+  static_assert((WVN & (WVN - 1)) == 0, "wave index split by shift and mask");
   static_assert(FM % 2 == 0, "the slice is split in halves by A block");
   static_assert(LDS_BYTES <= 163840, "160 KiB of LDS");
   static_assert(LDS == kLdsXor || LDS == kLdsPlain, "layouts of this kernel");
 };
 
 // Epilogue of a BM x BN tile whose FP32 sums a workgroup holds in acc (wave
-// w: block (w/2, w%2) of (BM/2) x (BN/2); lane l, tile (i, j): C[m][n .. n+3],
+// w: block (w/WVN, w%WVN) of WTM x WTN; lane l, tile (i, j): C[m][n .. n+3],
 // m = block row + 16i + l%16, n = block column + 16j + 4*(l/16)).
 // C = alpha * acc + beta * C, rounded once to the output type; with alpha ==
 // 1 and beta == 0 the sums are converted as they are and C is not read.
@@ -98,7 +105,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T:
                                            char *smem, int m0, int n0, int wave, int lane) {
   constexpr int FM = T::FM, FN = T::FN;
   const int M = args.M, N = args.N, ldc = args.ldc;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = (unsigned)wave / T::WVN, wn = (unsigned)wave % T::WVN;
   const int wm0 = m0 + wm * T::WTM, wn0 = n0 + wn * T::WTN;
   const float alpha = args.alpha, beta = args.beta;
   // packed output of tile (i, j) for this lane
@@ -222,7 +229,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   const int n0 = __builtin_amdgcn_readfirstlane(tn * BN);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = (unsigned)wave / T::WVN, wn = (unsigned)wave % T::WVN;
   const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
 
   // ---- direct-to-LDS loads ------------------------------------------------
@@ -486,7 +493,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
     // latency, so 24 wait states first: more than the 19 the slowest MFMA
     // needs before a memory instruction may read its result.)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-    float *dst = args.ws + ((size_t)slot * 4 + wave) * (FM * FN * 256) + lane * 4;
+    float *dst = args.ws + ((size_t)slot * T::NW + wave) * (FM * FN * 256) + lane * 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -514,7 +521,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
 enum LaunchMode { kWhole = 0, kSegments = 1, kMixed = 2 };
 
 template <class T, int LAYOUT, int DT, int MODE>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
+__global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
   const int b = blockIdx.x;
   if constexpr (MODE == kWhole) {
@@ -537,7 +544,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
 // Second half of a K-split launch: the S FP32 partial sums of each split tile
 // are added in segment order (so the result does not depend on which segment
 // finished first) and written to C with alpha and beta, rounded once.  A
-// tile's partial sums are 4*FM*FN chunks of 1 KiB (wave block, then MFMA tile
+// tile's partial sums are NW*FM*FN chunks of 1 KiB (wave block, then MFMA tile
 // (i, j); one accumulator quad per lane); workgroup b handles the 16 chunks
 // 16*(b % P) .. of split tile b / P, each thread 4 chunks of one lane, with the
 // loads of four segments in flight before they are added (the sums are
@@ -545,7 +552,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs args) {
 template <class T, int DT>
 __global__ __launch_bounds__(256) void gemm_sk_fixup(GemmArgs args) {
   constexpr int FM = T::FM, FN = T::FN;
-  constexpr int CHUNKS = 4 * FM * FN;
+  constexpr int CHUNKS = T::NW * FM * FN;
   constexpr int P = fixup_parts(T::BM, T::BN);
   static_assert(CHUNKS == 16 * P, "16 chunks a workgroup");
   constexpr int SLOT = CHUNKS * 256;  // floats of one segment's partial sums
@@ -584,8 +591,8 @@ __global__ __launch_bounds__(256) void gemm_sk_fixup(GemmArgs args) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int ch = c0 + c, w = ch / (FM * FN), ij = ch % (FM * FN);
-    const int m = tm * T::BM + (w >> 1) * T::WTM + (ij / FN) * 16 + (lane & 15);
-    const int n = tn * T::BN + (w & 1) * T::WTN + (ij % FN) * 16 + 4 * (lane >> 4);
+    const int m = tm * T::BM + ((unsigned)w / T::WVN) * T::WTM + (ij / FN) * 16 + (lane & 15);
+    const int n = tn * T::BN + ((unsigned)w % T::WVN) * T::WTN + (ij % FN) * 16 + 4 * (lane >> 4);
     if (m >= M || n >= N) continue;  // N % 8 == 0: n < N covers n .. n+3
     uint16_t *cp = args.C + (size_t)m * ldc + n;
     float x[4] = {acc[c][0], acc[c][1], acc[c][2], acc[c][3]};

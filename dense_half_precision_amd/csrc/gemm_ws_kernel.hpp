@@ -36,6 +36,7 @@ template <int BM_, int BN_>
 struct WsCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 64;
   static constexpr int NT = 512;                      // 4 MFMA waves (2 x 2) + 4 loader waves
+  static constexpr int WVM = 2, WVN = 2, NW = 4;      // the MFMA waves
   static constexpr int WTM = BM / 2, WTN = BN / 2;    // MFMA wave block
   static constexpr int FM = WTM / 16, FN = WTN / 16;  // 16x16 MFMA tiles per wave
   static constexpr int NMF = FM * FN;                 // MFMAs per 32-k slice

@@ -30,14 +30,15 @@ struct KernelEntry {
   kernel_fn split_fn;  // K segments of the tail tiles only (general kernels)
   kernel_fn mixed_fn;  // K segments, then whole tiles, in one launch (general kernels)
   kernel_fn fixup;     // adds the K segments of split tiles (general kernels)
-  int threads = 256;   // workgroup size
+  int threads = 256;   // workgroup size of fn, split_fn and mixed_fn
 };
+constexpr int kFixupThreads = 256;  // gemm_sk_fixup's workgroup size
 
 template <class T, int LAYOUT, int DT>
 constexpr KernelEntry entry(const char *name, int group_m, bool production) {
   return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, production, true,
                      &gemm_kernel<T, LAYOUT, DT, kWhole>, &gemm_kernel<T, LAYOUT, DT, kSegments>,
-                     &gemm_kernel<T, LAYOUT, DT, kMixed>, &gemm_sk_fixup<T, DT>};
+                     &gemm_kernel<T, LAYOUT, DT, kMixed>, &gemm_sk_fixup<T, DT>, T::NT};
 }
 // producer/consumer wave specialisation: leading dimensions, alpha and beta,
 // no K split; an ablation, never chosen automatically
@@ -58,6 +59,7 @@ using T128 = TileCfg<128, 128>;
 using T64 = TileCfg<64, 64>;
 using T128x256 = TileCfg<128, 256>;
 using W128x256 = WsCfg<128, 256>;
+using T256W2x4 = TileCfg<256, 256, kLdsXor, 1, 2, 4>;  // eight waves, two per SIMD
 using T256Plain = TileCfg<256, 256, kLdsPlain>;
 using T256Direct = TileCfg<256, 256, kLdsXor, 0>;
 using R256 = RsCfg<256, 256, 2, 2, kLdsXor>;
@@ -109,6 +111,9 @@ const KernelEntry kTable[] = {
     ws_entry<W128x256, kBF16>("ws_tn_bf16_128x256x64", 4),
     entry<T128x256, kTN, kF16>("tn_f16_128x256x64", 4, false),
     entry<T128x256, kTN, kBF16>("tn_bf16_128x256x64", 4, false),
+    // the 256 x 256 tile on eight waves (two per SIMD)
+    entry<T256W2x4, kTN, kF16>("tn_f16_256x256x64_w2x4", 4, false),
+    entry<T256W2x4, kTN, kBF16>("tn_bf16_256x256x64_w2x4", 4, false),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -261,8 +266,7 @@ hgemm_status_t validate(const Call &c) {
   return HGEMM_OK;
 }
 
-hgemm_status_t launch(kernel_fn fn, int64_t grid, const GemmArgs &a, void *stream,
-                      int threads = 256) {
+hgemm_status_t launch(kernel_fn fn, int64_t grid, const GemmArgs &a, void *stream, int threads) {
   // hipGetLastError() reports the last error of any earlier runtime call on
   // this thread too: clear it so that only the launch's own result is seen
   (void)hipGetLastError();
@@ -347,14 +351,14 @@ hgemm_status_t run(const Call &c, void *stream, const hgemm_config_t *cfg) {
   const int64_t nseg = plan.sk_tiles * plan.split;
   if (plan.dp_tiles > 0) {
     a.grid = (int)plan.dp_tiles;
-    st = launch(e.mixed_fn, plan.dp_tiles + nseg, a, stream);
+    st = launch(e.mixed_fn, plan.dp_tiles + nseg, a, stream, e.threads);
   } else {
     a.grid = (int)nseg;
-    st = launch(e.split_fn, nseg, a, stream);
+    st = launch(e.split_fn, nseg, a, stream, e.threads);
   }
   if (st != HGEMM_OK) return st;
   a.grid = (int)plan.sk_tiles * fixup_parts(e.bm, e.bn);
-  return launch(e.fixup, a.grid, a, stream);
+  return launch(e.fixup, a.grid, a, stream, kFixupThreads);
 }
 
 // The pages' two layouts: packed storage, alpha 1, beta 0.

@@ -101,7 +101,8 @@ def test_every_transposed_a_kernel_ragged(kernel):
 @pytest.mark.parametrize("name", ["tn_f16_256x256x64", "nn_bf16_256x256x64", "tn_bf16_128x128x64",
                                   "nn_f16_64x64x64", "tn_f16_256x256x64_directepi",
                                   "ws_tn_f16_128x256x64", "ws_tn_bf16_128x256x64",
-                                  "tn_f16_128x256x64"])
+                                  "tn_f16_128x256x64", "tn_f16_256x256x64_w2x4",
+                                  "tn_bf16_256x256x64_w2x4"])
 def test_general_form_on_tn_nn_kernels(name):
     """Leading dimensions, alpha and beta through the TN/NN kernels."""
     k = hgemm.kernel_table()[hgemm.kernel_index(name)]

@@ -117,3 +117,26 @@ def test_split_deterministic_and_small_workspace():
     r, c = inputs.stratified_samples(M, N, 63)
     ref = oracle.gemm_sampled(0, 1, dt, M, N, K, A, Bt, r, c, 1.0, 0.0)
     helpers.parity(g1[r, c], ref, dt, "automatic split 4352^2 x 4096")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_split_eight_wave_kernel(dt):
+    """The 256 x 256 tile on eight waves (2 x 4 wave blocks of 128 x 64): its
+    segments store partial sums in eight wave blocks, which the fixup maps
+    back to C.  Forced split, whole rounds plus a tail (4352^2: 289 tiles),
+    alpha/beta, K tail; sampled elements against the oracle, and the whole
+    output against the four-wave kernel's split call."""
+    M = N = 4352
+    K = 1000
+    name = f"tn_{dt}_256x256x64_w2x4"
+    k8 = hgemm.kernel_index(name)
+    k4 = hgemm.kernel_index(f"tn_{dt}_256x256x64")
+    As, Bs, Cs = _operands(dt, 0, 1, M, N, K, 11, 0, 0)
+    ws = 33 * 5 * 262144
+    got = helpers.gpu_gemm_ws(0, 1, dt, M, N, K, As, Bs, 0.75, -0.5, Cs, ws, split=5, kernel=k8)
+    four = helpers.gpu_gemm_ws(0, 1, dt, M, N, K, As, Bs, 0.75, -0.5, Cs, ws, split=5, kernel=k4)
+    r, c = inputs.stratified_samples(M, N, 12)
+    ref = oracle.gemm_sampled(0, 1, dt, M, N, K, As, Bs, r, c, 0.75, -0.5, Cs)
+    helpers.parity(got[r, c], ref, dt, f"{name} split 5")
+    # same tile, same K segments, same order of the FP32 sums: the same bits
+    assert np.array_equal(got, four), f"{name}: split result differs from the four-wave kernel's"
