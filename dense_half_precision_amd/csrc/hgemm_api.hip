@@ -135,13 +135,11 @@ int find_kernel(int layout, int dtype, int bm) {
   return -1;
 }
 
-// Estimated times, in units of one 256 x 256 x 64 tile step at full rate
-// (about 1.3 us on MI355X): a launch of square tiles of size t runs
-// ceil(tiles / 256 CUs) waves of one workgroup per CU, each tile taking
-// KT * (t/256)^2 / rate_t units, rate_t the per-CU throughput of that tile size
-// at full occupancy relative to the 256 kernel (128: 0.8, 64: 0.5, measured).
 // Cost model of the automatic choice, in units of one K step of a 256 x 256
-// tile on every CU at once (about 1.3 us on this chip); the constants were
+// tile on every CU at once (about 1.3 us on MI355X).  A launch of square tiles
+// of size t runs ceil(tiles / 256 CUs) rounds of one workgroup per CU, each
+// tile taking (KT + kTileFixed) * (t/256)^2 / rate_t units, rate_t the per-CU
+// throughput of that tile size relative to the 256 kernel.  The constants were
 // chosen on measured times of every tile size and split over square, skinny
 // and long-K shapes.
 constexpr int64_t kCUs = 256;
@@ -470,7 +468,6 @@ const char *hgemm_kernel_info(int index, int *layout, int *dtype, int *bm, int *
 }
 
 int hgemm_auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K) {
-  (void)K;
   if (layout < kTN || layout > kAtNN || (dtype != HGEMM_F16 && dtype != HGEMM_BF16) || M <= 0 ||
       N <= 0)
     return -1;

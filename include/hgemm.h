@@ -214,9 +214,11 @@ const char *hgemm_kernel_info(int index, int *layout, int *dtype, int *bm,
 
 /* Kernel table index the automatic choice would use for this call (layout
  * as in hgemm_kernel_info), or -1 for invalid arguments.  The choice takes the tile
- * size (256, 128 or 64, square) with the least estimated time: waves of
- * workgroups over the 256 CUs times one tile's area over that tile size's
- * relative throughput (1, 0.8, 0.5); ties go to the larger tile. */
+ * size (256, 128 or 64, square) with the least estimated time: rounds of
+ * workgroups over the 256 CUs, times the K steps of 64 plus 3 for a tile's
+ * prologue and epilogue, times the tile's area over that tile size's relative
+ * throughput (1, 0.8, 0.5); ties go to the larger tile.  This is the choice
+ * of hgemm_tn, hgemm_nn and hgemm_gemm; hgemm_gemm_ws may split K instead. */
 int hgemm_auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus
