@@ -225,6 +225,83 @@ def micro() -> int:
     return 0
 
 
+def compare() -> int:
+    """This library's automatic choice against torch.mm (the vendor library) on
+    the five workloads, one JSON line each, measured two ways: one launch at a
+    time (an event pair around each launch and a wait for it: launch latency
+    included), and back to back (wall clock over many launches, no events: the
+    rate a caller that enqueues without waiting sees).  The two libraries
+    alternate, round by round, so that clock drift under the power cap falls
+    on both alike."""
+    import time
+    import numpy as np
+    import torch
+    from dense_half_precision_amd import hgemm, inputs
+    lib = hgemm.lib()
+    sp = torch.cuda.current_stream().cuda_stream
+
+    def one_at_a_time(f, n):
+        for _ in range(n // 4):
+            f()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return ts
+
+    def back_to_back(f, n):
+        for _ in range(n // 4):
+            f()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            f()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n
+
+    for widx in (1, 2, 3, 4, 5):
+        w = inputs.workload(widx)
+        A, B = inputs.operands(w)
+        dA = torch.from_numpy(A.view(np.int16)).cuda()
+        dB = torch.from_numpy(B.view(np.int16)).cuda()
+        dC = torch.empty((w.M, w.N), dtype=torch.int16, device="cuda")
+        cfn = lib.hgemm_tn if w.layout == "tn" else lib.hgemm_nn
+        args = (w.M, w.N, w.K, hgemm.F16 if w.dtype == "f16" else hgemm.BF16,
+                dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), sp)
+
+        def ours():
+            st = cfn(*args)
+            if st != hgemm.OK:
+                raise hgemm.HgemmError(st, "compare launch")
+
+        tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+        a, b = dA.view(tdt), dB.view(tdt)
+        vendor = (lambda: torch.mm(a, b.t())) if w.layout == "tn" else (lambda: torch.mm(a, b))
+        n = 1000 if w.M <= 2048 else 50
+        res = {"ours": ([], []), "torch.mm": ([], [])}
+        for _ in range(4):
+            for name, f in (("ours", ours), ("torch.mm", vendor)):
+                res[name][0].extend(one_at_a_time(f, n))
+                res[name][1].append(back_to_back(f, n))
+        kern = hgemm.kernel_table()[hgemm.auto_kernel(
+            hgemm.TN if w.layout == "tn" else hgemm.NN, w.dtype, w.M, w.N, w.K)]["name"]
+        line = {"compare": w.name, "kernel": kern}
+        for name, (single, b2b) in res.items():
+            t1, t2 = float(np.median(single)), float(np.median(b2b))
+            line[name] = {"one_at_a_time_us": round(t1 * 1e6, 2),
+                          "one_at_a_time_tflops": round(w.flops / t1 / 1e12, 1),
+                          "back_to_back_us": round(t2 * 1e6, 2),
+                          "back_to_back_tflops": round(w.flops / t2 / 1e12, 1)}
+        print(json.dumps(line), flush=True)
+        del dA, dB, dC
+    return 0
+
+
 TAIL_SHAPES = [  # (layout, dtype, M, N, K): tiles of 256 x 256 that leave a partial round
     ("tn", "f16", 6144, 6144, 6144), ("nn", "bf16", 6144, 6144, 6144),
     ("tn", "f16", 7168, 7168, 7168), ("tn", "f16", 4352, 4352, 4096),
@@ -309,6 +386,9 @@ def main() -> int:
                     help="K split of the tail vs the unsplit choice and torch.mm, per shape")
     ap.add_argument("--vendor", action="store_true",
                     help="run the workload through torch.mm (the vendor library) instead")
+    ap.add_argument("--compare", action="store_true",
+                    help="automatic choice vs torch.mm on every workload, one launch at a "
+                         "time and back to back")
     ap.add_argument("--oracle-table", action="store_true",
                     help="time the CPU oracle on every workload (host only) and exit")
     args = ap.parse_args()
@@ -324,6 +404,11 @@ def main() -> int:
             print("bench.py: one GPU only", file=sys.stderr)
             return 2
         return micro()
+    if args.compare:
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            return 2
+        return compare()
 
     if args.gpus != 1:
         print(f"bench.py: this HGEMM runs on one GPU; --gpus {args.gpus} is not supported "

@@ -18,12 +18,13 @@
 // 1 KiB segment per wave instruction, no registers involved (the pages'
 // asynchronous gmem -> smem copies: cp.async in the HGEMM MMA note's main
 // loop section, TMA in the tcgen05 translation).  Rows past M/N and k past K
-// read as zero through the buffer range check.  The LDS holds a ring of three
-// A stages and two B stages (A and B of one K step of 64 are 32 KiB each for
-// a 256 x 256 tile, 160 KiB in all): the loads of A run two steps ahead and
-// the loads of B one step ahead -- the multi-stage pipeline of the HGEMM MMA
-// note and of the tcgen05 translation's pipelining section, sized to the
-// 160 KiB LDS of gfx950.  Each 128-byte row of a K step is stored with its
+// read as zero through the buffer range check.  The LDS holds a ring of NSB
+// + 1 A stages and NSB B stages, three and two for a 256 x 256 tile (A and B
+// of one K step of 64 are 32 KiB each there, 160 KiB in all): the loads of
+// step s are issued during step s - NSB, those of A before that step's
+// barrier and those of B after it -- the multi-stage pipeline of the HGEMM MMA note and
+// of the tcgen05 translation's pipelining section, sized to the 160 KiB LDS of
+// gfx950.  Each 128-byte row of a K step is stored with its
 // 16-byte chunks XOR-swizzled (chunk ^ ((row >> 1) & 7)), an LDS layout that
 // keeps both the 16-byte fragment reads and the direct-to-LDS writes free of
 // bank conflicts (the swizzle of the CuTe note's first step and the ablation
@@ -66,10 +67,14 @@
 
 namespace hgemm {
 
-template <int BM_, int BN_, int LDS_ = kLdsXor, int EPI_ = 1, int WVM_ = 2, int WVN_ = 2>
+template <int BM_, int BN_, int LDS_ = kLdsXor, int EPI_ = 1, int WVM_ = 2, int WVN_ = 2,
+          int NSB_ = 2>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 64;
   static constexpr int WVM = WVM_, WVN = WVN_;        // waves along M and N
+  // LDS ring: NSA stages of A and NSB of B; A is loaded NSA - 1 steps ahead
+  // (in slice 0), B NSB steps ahead (after the barrier)
+  static constexpr int NSB = NSB_, NSA = NSB_ + 1;
   static constexpr int NW = WVM * WVN;                // waves per workgroup
   static constexpr int NT = 64 * NW;
   static constexpr int WTM = BM / WVM, WTN = BN / WVN;  // wave block
@@ -79,8 +84,8 @@ struct TileCfg {
   static constexpr int EPI = EPI_;                    // 1: C through LDS, 0: direct stores
   static constexpr int A_STAGE = BM * 128;            // BM rows x 64 k x 2 bytes
   static constexpr int B_STAGE = BN * 128;            // TN: BN rows x 64 k; NN: 64 rows x BN
-  static constexpr int B_BASE = 3 * A_STAGE;          // three A stages, then two B stages
-  static constexpr int PIPE_BYTES = 3 * A_STAGE + 2 * B_STAGE;
+  static constexpr int B_BASE = NSA * A_STAGE;        // the A stages, then the B stages
+  static constexpr int PIPE_BYTES = NSA * A_STAGE + NSB * B_STAGE;
   static constexpr int CROW = WTN * 2 + 16;           // epilogue row pitch (bytes)
   static constexpr int EPI_BYTES = EPI ? NW * WTM * CROW : 0;
   static constexpr int LDS_BYTES = PIPE_BYTES > EPI_BYTES ? PIPE_BYTES : EPI_BYTES;
@@ -264,9 +269,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   const uint16_t *b_panel =
       B_MN ? args.B + n0 + (size_t)k_begin * ldb : args.B + (size_t)n0 * ldb + k_begin;
 
-  // A stage of step s at (s % 3) * A_STAGE, B stage at B_BASE + (s & 1) * B_STAGE
-  auto a_base = [&](int s) { return (uint32_t)((s % 3) * T::A_STAGE); };
-  auto b_base = [&](int s) { return (uint32_t)(T::B_BASE + (s & 1) * T::B_STAGE); };
+  // A stage of step s at (s % NSA) * A_STAGE, B stage at B_BASE + (s % NSB) * B_STAGE
+  constexpr int NSA = T::NSA, NSB = T::NSB;
+  auto a_base = [&](int s) { return (uint32_t)((s % NSA) * T::A_STAGE); };
+  auto b_base = [&](int s) { return (uint32_t)(T::B_BASE + (s % NSB) * T::B_STAGE); };
+  // Loads still in flight at each step's barrier: those issued after the B
+  // loads of step kt+1 (A of NSB-1 later steps, B of NSB-2), which the wait
+  // there lets run on.
+  constexpr int AHEAD = (NSB - 1) * SEG_A + (NSB - 2) * SEG_B;
+  static_assert(AHEAD < 64, "vmcnt range");
 
   // Buffer resource of one operand for the K step starting at k0: rows past
   // the tile edge (k-contiguous) or k-rows past this workgroup's K range
@@ -391,40 +402,46 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
 
   const int KT = (K + BK - 1) / BK;
 
-  // ---- prologue: A of steps 0, 1 and B of step 0 in flight; slice 0 read ----
-  if (tail == 0) mask_tail();
-  prep_a(0);
+  // ---- prologue: the loads the loop's earlier steps would have issued, in
+  // the same order (A of step s, then B of step s, for s = 0 .. NSB-1), the
+  // last B after the first barrier, where it overlaps the reads of slice 0 ----
 #pragma unroll
-  for (int i = 0; i < SEG_A; ++i) load_a(a_base(0), i);
-  prep_b(0);
+  for (int st = 0; st < NSB; ++st) {
+    if (tail == st) mask_tail();
+    prep_a(st);
 #pragma unroll
-  for (int i = 0; i < SEG_B; ++i) load_b(b_base(0), i);
-  if (tail == 1) mask_tail();
-  prep_a(1);
+    for (int i = 0; i < SEG_A; ++i) load_a(a_base(st), i);
+    if (st < NSB - 1) {
+      prep_b(st);
 #pragma unroll
-  for (int i = 0; i < SEG_A; ++i) load_a(a_base(1), i);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(SEG_A, 0));
+      for (int i = 0; i < SEG_B; ++i) load_b(b_base(st), i);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(AHEAD, 0));  // step 0 in LDS
   wg_barrier();
-  prep_b(1);
+  prep_b(NSB - 1);
 #pragma unroll
   for (int q = 0; q < NR; ++q) {
     read_op(I0{}, a_base(0), b_base(0), 0, q);
-    if (q * SEG_B / NR != (q + 1) * SEG_B / NR) load_b(b_base(1), q * SEG_B / NR);
+    if (q * SEG_B / NR != (q + 1) * SEG_B / NR) load_b(b_base(NSB - 1), q * SEG_B / NR);
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- main loop -------------------------------------------------------------
-  // stage offsets of steps kt, kt+1, kt+2, rotated at the end of each step
-  // (no division by 3 in the loop)
-  uint32_t ra0 = a_base(0), ra1 = a_base(1), ra2 = a_base(2);
-  uint32_t rb0 = b_base(0), rb1 = b_base(1);
+  // stage offsets of steps kt, kt+1, ..., rotated at the end of each step
+  // (no division in the loop); ra[NSA-1] is also the stage of step kt-1
+  uint32_t ra[NSA], rb[NSB];
+#pragma unroll
+  for (int i = 0; i < NSA; ++i) ra[i] = a_base(i);
+#pragma unroll
+  for (int i = 0; i < NSB; ++i) rb[i] = b_base(i);
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 2 == tail) mask_tail();  // loads of steps kt+2 on are issued below
-    const uint32_t ca = ra0, cb = rb0;
-    const uint32_t na = ra1, nb = rb1;
-    // X: slice 0; read slice 1; A of step kt+2 into the stage step kt-1 used
-    prep_a(kt + 2);
-    const uint32_t la = ra2;
+    if (kt + NSB == tail) mask_tail();  // loads of steps kt+NSB on are issued below
+    const uint32_t ca = ra[0], cb = rb[0];
+    const uint32_t na = ra[1], nb = rb[1];
+    // X: slice 0; read slice 1; A of step kt+NSA-1 into the stage step kt-1 used
+    prep_a(kt + NSA - 1);
+    const uint32_t la = ra[NSA - 1];
     wait_set(I0{});
 #pragma unroll
     for (int t = 0; t < NMF; ++t) {
@@ -444,12 +461,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
       mfma(I1{}, t);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // step kt+1 complete in LDS (A of kt+2 may stay in flight), own reads done
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(SEG_A, 0));
+    // step kt+1 complete in LDS (later steps' loads may stay in flight), own
+    // reads done
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(AHEAD, 0));
     wg_barrier();
-    // Z: second half of slice 1; read slice 0 of step kt+1; B of step kt+2
-    prep_b(kt + 2);
-    const uint32_t lb = rb0;  // step kt+2 reuses the B stage of step kt
+    // Z: second half of slice 1; read slice 0 of step kt+1; B of step kt+NSB
+    prep_b(kt + NSB);
+    const uint32_t lb = rb[0];  // step kt+NSB reuses the B stage of step kt
 #pragma unroll
     for (int t = NMF / 2; t < NMF; ++t) {
       mfma(I1{}, t);
@@ -463,12 +481,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    const uint32_t r = ra0;
-    ra0 = ra1;
-    ra1 = ra2;
-    ra2 = r;
-    rb0 = rb1;
-    rb1 = cb;
+#pragma unroll
+    for (int i = 0; i < NSA - 1; ++i) ra[i] = ra[i + 1];
+    ra[NSA - 1] = ca;
+#pragma unroll
+    for (int i = 0; i < NSB - 1; ++i) rb[i] = rb[i + 1];
+    rb[NSB - 1] = cb;
   }
 
   // The last step (or, for K = 0, the prologue) read fragments for a step that

@@ -31,6 +31,7 @@ struct KernelEntry {
   kernel_fn mixed_fn;  // K segments, then whole tiles, in one launch (general kernels)
   kernel_fn fixup;     // adds the K segments of split tiles (general kernels)
   int threads = 256;   // workgroup size of fn, split_fn and mixed_fn
+  int nsb = 2;         // B stages of the LDS ring (A has one more)
 };
 constexpr int kFixupThreads = 256;  // gemm_sk_fixup's workgroup size
 
@@ -38,7 +39,14 @@ template <class T, int LAYOUT, int DT>
 constexpr KernelEntry entry(const char *name, int group_m, bool production) {
   return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, production, true,
                      &gemm_kernel<T, LAYOUT, DT, kWhole>, &gemm_kernel<T, LAYOUT, DT, kSegments>,
-                     &gemm_kernel<T, LAYOUT, DT, kMixed>, &gemm_sk_fixup<T, DT>, T::NT};
+                     &gemm_kernel<T, LAYOUT, DT, kMixed>, &gemm_sk_fixup<T, DT>, T::NT, T::NSB};
+}
+// whole-K tiles only (no K-split instantiations)
+template <class T, int LAYOUT, int DT>
+constexpr KernelEntry dp_entry(const char *name, int group_m, bool production) {
+  return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, production, true,
+                     &gemm_kernel<T, LAYOUT, DT, kWhole>, nullptr, nullptr, nullptr, T::NT,
+                     T::NSB};
 }
 // producer/consumer wave specialisation: leading dimensions, alpha and beta,
 // no K split; an ablation, never chosen automatically
@@ -60,6 +68,7 @@ using T64 = TileCfg<64, 64>;
 using T128x256 = TileCfg<128, 256>;
 using W128x256 = WsCfg<128, 256>;
 using T256W2x4 = TileCfg<256, 256, kLdsXor, 1, 2, 4>;  // eight waves, two per SIMD
+using T128R3 = TileCfg<128, 128, kLdsXor, 1, 2, 2, 3>;  // 4 A + 3 B stages, 112 KiB
 using T256Plain = TileCfg<256, 256, kLdsPlain>;
 using T256Direct = TileCfg<256, 256, kLdsXor, 0>;
 using R256 = RsCfg<256, 256, 2, 2, kLdsXor>;
@@ -114,6 +123,15 @@ const KernelEntry kTable[] = {
     // the 256 x 256 tile on eight waves (two per SIMD)
     entry<T256W2x4, kTN, kF16>("tn_f16_256x256x64_w2x4", 4, false),
     entry<T256W2x4, kTN, kBF16>("tn_bf16_256x256x64_w2x4", 4, false),
+    // the 128 x 128 tile with a deeper LDS ring, for a single round of tiles
+    dp_entry<T128R3, kTN, kF16>("tn_f16_128x128x64_r3", 4, true),
+    dp_entry<T128R3, kTN, kBF16>("tn_bf16_128x128x64_r3", 4, true),
+    dp_entry<T128R3, kNN, kF16>("nn_f16_128x128x64_r3", 4, true),
+    dp_entry<T128R3, kNN, kBF16>("nn_bf16_128x128x64_r3", 4, true),
+    dp_entry<T128R3, kAtTN, kF16>("at_tn_f16_128x128x64_r3", 4, true),
+    dp_entry<T128R3, kAtTN, kBF16>("at_tn_bf16_128x128x64_r3", 4, true),
+    dp_entry<T128R3, kAtNN, kF16>("at_nn_f16_128x128x64_r3", 4, true),
+    dp_entry<T128R3, kAtNN, kBF16>("at_nn_bf16_128x128x64_r3", 4, true),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -127,10 +145,10 @@ constexpr int64_t kMaxLdK = int64_t(1) << 22;
 constexpr int64_t kMaxLdMN = int64_t(1) << 23;
 constexpr int64_t kMaxLdC = (int64_t(1) << 31) - 8;
 
-int find_kernel(int layout, int dtype, int bm) {
+int find_kernel(int layout, int dtype, int bm, int nsb = 2) {
   for (int i = 0; i < kTableSize; ++i)
     if (kTable[i].production && kTable[i].layout == layout && kTable[i].dtype == dtype &&
-        kTable[i].bm == bm)
+        kTable[i].bm == bm && kTable[i].nsb == nsb)
       return i;
   return -1;
 }
@@ -159,12 +177,20 @@ double dp_cost(int i, int64_t M, int64_t N, int64_t KT) {
 }
 
 // Automatic choice without a K split: the tile size with the least estimated
-// time; ties go to the larger tile.
+// time; ties go to the larger tile.  A single round of 128 x 128 tiles over at
+// least kDeepRingSteps K steps takes the ring with one more stage per operand:
+// one workgroup per CU either way, and the deeper prefetch hides the load
+// latency (measured 3-17 % faster there).  With more than one round two
+// workgroups share a CU, which the deeper ring's LDS would forbid.
+constexpr int64_t kDeepRingSteps = 24;
 int auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K) {
   const int64_t KT = K > 0 ? (K + 63) / 64 : 1;
   int best = 0;
   for (int i = 1; i < 3; ++i)
     if (dp_cost(i, M, N, KT) < dp_cost(best, M, N, KT)) best = i;
+  const int64_t t = kSizes[best];
+  if (t == 128 && ((M + t - 1) / t) * ((N + t - 1) / t) <= kCUs && KT >= kDeepRingSteps)
+    return find_kernel(layout, dtype, 128, 3);
   return find_kernel(layout, dtype, kSizes[best]);
 }
 

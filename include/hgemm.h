@@ -217,8 +217,11 @@ const char *hgemm_kernel_info(int index, int *layout, int *dtype, int *bm,
  * size (256, 128 or 64, square) with the least estimated time: rounds of
  * workgroups over the 256 CUs, times the K steps of 64 plus 3 for a tile's
  * prologue and epilogue, times the tile's area over that tile size's relative
- * throughput (1, 0.8, 0.5); ties go to the larger tile.  This is the choice
- * of hgemm_tn, hgemm_nn and hgemm_gemm; hgemm_gemm_ws may split K instead. */
+ * throughput (1, 0.8, 0.5); ties go to the larger tile.  A single round of
+ * 128 x 128 tiles (at most 256) over 24 or more K steps takes that tile's
+ * entry with one more LDS stage per operand (the "_r3" names).  This is the
+ * choice of hgemm_tn, hgemm_nn and hgemm_gemm; hgemm_gemm_ws may split K
+ * instead. */
 int hgemm_auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus

@@ -163,6 +163,12 @@ def test_kernel_table_and_auto_choice():
     assert tab[hgemm.auto_kernel(0, 0, 8192, 8192, 8192)]["bm"] == 256
     assert tab[hgemm.auto_kernel(1, 1, 4096, 4096, 4096)]["bm"] == 256
     assert tab[hgemm.auto_kernel(0, 0, 2048, 2048, 2048)]["bm"] == 128
+    # one round of 128 x 128 tiles (at most 256) over 24 or more K steps takes
+    # the ring with one more stage per operand; more rounds, or fewer steps, not
+    assert tab[hgemm.auto_kernel(0, 0, 2048, 2048, 2048)]["name"] == "tn_f16_128x128x64_r3"
+    assert tab[hgemm.auto_kernel(3, 1, 1536, 1536, 1536)]["name"] == "at_nn_bf16_128x128x64_r3"
+    assert tab[hgemm.auto_kernel(1, 1, 2048, 2048, 1472)]["name"] == "nn_bf16_128x128x64"
+    assert tab[hgemm.auto_kernel(0, 0, 1024, 8192, 8192)]["name"] == "tn_f16_128x128x64"
 
 
 @pytest.mark.parametrize("tiles_m,tiles_n", [(1, 1), (2, 2), (3, 5), (32, 32), (16, 16), (8, 8),

@@ -82,6 +82,22 @@ def test_every_kernel_ragged(kernel):
         helpers.parity(C, oracle.hgemm(layout, dtype, A, B), dtype, f"{k['name']} gm={gm} xcd={xcd}")
 
 
+@pytest.mark.parametrize("name", ["tn_f16_128x128x64_r3", "nn_bf16_128x128x64_r3"])
+def test_deep_ring_k_tails(name):
+    """The 128 x 128 kernel with four A and three B LDS stages loads three
+    steps ahead: K of one to six steps puts the partial last step at each of
+    the prologue's loads and at the loop's, with ragged M and N."""
+    k = hgemm.kernel_table()[hgemm.kernel_index(name)]
+    layout = "tn" if k["layout"] == hgemm.TN else "nn"
+    dtype = "f16" if k["dtype"] == hgemm.F16 else "bf16"
+    w = inputs.Workload(0, layout, dtype, 0, 0, 0, "uniform")
+    for s, K in enumerate((8, 72, 136, 200, 264, 328, 64, 192)):
+        M, N = 200 + s, 136 + 8 * s
+        A, B = inputs.operands(w, M, N, K, seed_offset=40 + s)
+        C = helpers.gpu_gemm(layout, dtype, A, B, kernel=k["index"])
+        helpers.parity(C, oracle.hgemm(layout, dtype, A, B), dtype, f"{name} {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("layout", ["tn", "nn"])
 def test_k_zero_writes_zeros(layout):
     M, N = 40, 48
