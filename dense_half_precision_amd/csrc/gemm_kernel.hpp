@@ -56,9 +56,10 @@
 // the tcgen05 translation's 2-SM section).
 //
 // Launch modes (gemm_kernel's last parameter): whole-K tiles; K segments of
-// the tail tiles, whose FP32 partial sums gemm_sk_fixup adds up; or the whole
-// rounds followed by the segments in one launch.  A segment runs the same
-// tile code on a K sub-range.
+// the tail tiles, whose FP32 partial sums gemm_sk_fixup adds up; the whole
+// rounds followed by the segments in one launch; or one workgroup per CU
+// looping over whole-K tiles.  A segment runs the same tile code on a K
+// sub-range.
 #pragma once
 
 #include <type_traits>
@@ -192,7 +193,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T:
 // SPLIT: only K segment `seg` of sk_split, whose FP32 partial sums go to
 // workspace slot `slot` (a separate instantiation, so that whole-K tiles
 // carry none of the segment bookkeeping in registers).
-template <class T, int LAYOUT, int DT, bool SPLIT>
+template <class T, int LAYOUT, int DT, bool SPLIT, bool OPAQUE = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int tile, int seg,
                                           int slot) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
@@ -232,7 +233,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   // load into a per-lane loop)
   const int m0 = __builtin_amdgcn_readfirstlane(tm * BM);
   const int n0 = __builtin_amdgcn_readfirstlane(tn * BN);
-  const int tid = threadIdx.x, lane = tid & 63;
+  int tid = threadIdx.x;
+  // called in a loop over tiles: hide the thread index, so that per-lane
+  // offsets are recomputed per tile instead of being kept live across the
+  // epilogue
+  if constexpr (OPAQUE) asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = (unsigned)wave / T::WVN, wn = (unsigned)wave % T::WVN;
   const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
@@ -536,7 +542,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
 //     short segments fill the CUs as the last whole tiles finish, with no
 //     launch boundary between them, and their partial sums are written last,
 //     while the caches still hold them for the fixup.
-enum LaunchMode { kWhole = 0, kSegments = 1, kMixed = 2 };
+//   kPersistent: whole-K tiles, gridDim.x workgroups (one per CU) each taking
+//     positions b, b + gridDim.x, ... of `grid`: the same tile on the same XCD
+//     in the same round as kWhole, but the next tile's loads start while the
+//     last one's stores of C drain, and no workgroup is launched per tile.
+enum LaunchMode { kWhole = 0, kSegments = 1, kMixed = 2, kPersistent = 3 };
 
 template <class T, int LAYOUT, int DT, int MODE>
 __global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs args) {
@@ -545,6 +555,15 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs args) {
   if constexpr (MODE == kWhole) {
     const int p = __builtin_amdgcn_readfirstlane(xcd_position(b, args.grid, args.xcd_remap));
     gemm_tile<T, LAYOUT, DT, false>(args, smem, args.tile_begin + p, 0, 0);
+  } else if constexpr (MODE == kPersistent) {
+    for (int v = b; v < args.grid; v += gridDim.x) {
+      const int p = __builtin_amdgcn_readfirstlane(xcd_position(v, args.grid, args.xcd_remap));
+      gemm_tile<T, LAYOUT, DT, false, true>(args, smem, args.tile_begin + p, 0, 0);
+      // every wave has read its epilogue rows back from LDS before the next
+      // tile's loads overwrite them (the stores of C may still be in flight)
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+      wg_barrier();
+    }
   } else {
     const int dp = MODE == kMixed ? args.grid : 0;  // whole tiles ahead of the segments
     if (MODE == kMixed && b < dp) {

@@ -32,6 +32,7 @@ struct KernelEntry {
   kernel_fn fixup;     // adds the K segments of split tiles (general kernels)
   int threads = 256;   // workgroup size of fn, split_fn and mixed_fn
   int nsb = 2;         // B stages of the LDS ring (A has one more)
+  bool persistent = false;  // fn runs one workgroup per CU over all tiles
 };
 constexpr int kFixupThreads = 256;  // gemm_sk_fixup's workgroup size
 
@@ -40,6 +41,13 @@ constexpr KernelEntry entry(const char *name, int group_m, bool production) {
   return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, production, true,
                      &gemm_kernel<T, LAYOUT, DT, kWhole>, &gemm_kernel<T, LAYOUT, DT, kSegments>,
                      &gemm_kernel<T, LAYOUT, DT, kMixed>, &gemm_sk_fixup<T, DT>, T::NT, T::NSB};
+}
+// persistent: one workgroup per CU loops over the tiles (whole K)
+template <class T, int LAYOUT, int DT>
+constexpr KernelEntry persistent_entry(const char *name, int group_m, bool production) {
+  return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, production, true,
+                     &gemm_kernel<T, LAYOUT, DT, kPersistent>, nullptr, nullptr, nullptr, T::NT,
+                     T::NSB, true};
 }
 // whole-K tiles only (no K-split instantiations)
 template <class T, int LAYOUT, int DT>
@@ -132,6 +140,10 @@ const KernelEntry kTable[] = {
     dp_entry<T128R3, kAtTN, kBF16>("at_tn_bf16_128x128x64_r3", 4, true),
     dp_entry<T128R3, kAtNN, kF16>("at_nn_f16_128x128x64_r3", 4, true),
     dp_entry<T128R3, kAtNN, kBF16>("at_nn_bf16_128x128x64_r3", 4, true),
+    // the 256 x 256 kernel as a persistent launch
+    persistent_entry<T256, kTN, kF16>("tn_f16_256x256x64_persist", 4, false),
+    persistent_entry<T256, kTN, kBF16>("tn_bf16_256x256x64_persist", 4, false),
+    persistent_entry<T256, kNN, kBF16>("nn_bf16_256x256x64_persist", 4, false),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -365,7 +377,9 @@ hgemm_status_t run(const Call &c, void *stream, const hgemm_config_t *cfg) {
   a.sk_split = 0;
   a.sk_tiles = 0;
   a.ws = nullptr;
-  if (plan.split == 0) return launch(e.fn, tiles, a, stream, e.threads);
+  if (plan.split == 0)
+    return launch(e.fn, e.persistent ? std::min<int64_t>(tiles, kCUs) : tiles, a, stream,
+                  e.threads);
   // the whole rounds' tiles and the tail's K segments in one launch (the
   // segments alone when there is no whole round), then the sums
   a.tile_begin = (int)plan.dp_tiles;

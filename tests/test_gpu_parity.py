@@ -98,6 +98,28 @@ def test_deep_ring_k_tails(name):
         helpers.parity(C, oracle.hgemm(layout, dtype, A, B), dtype, f"{name} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("name", ["tn_f16_256x256x64_persist", "nn_bf16_256x256x64_persist"])
+def test_persistent_many_tiles(name):
+    """The persistent launch (one workgroup per CU looping over tiles): 4352 x
+    4360 is 18 x 18 = 324 tiles, so 68 workgroups take a second tile, the last
+    row and column ragged, with a K tail; whole output by projection, a
+    stratified sample element by element, and the same bits as the plain
+    launch of the same tile code."""
+    k = hgemm.kernel_table()[hgemm.kernel_index(name)]
+    layout = "tn" if k["layout"] == hgemm.TN else "nn"
+    dtype = "f16" if k["dtype"] == hgemm.F16 else "bf16"
+    M, N, K = 4352 + 40, 4360, 712
+    w = inputs.Workload(0, layout, dtype, 0, 0, 0, "uniform")
+    A, B = inputs.operands(w, M, N, K, seed_offset=77)
+    C = helpers.gpu_gemm(layout, dtype, A, B, kernel=k["index"])
+    helpers.freivalds(C, A, B, layout, dtype)
+    r, c = inputs.stratified_samples(M, N, 78)
+    ref = oracle.hgemm_sampled(layout, dtype, A, B, r, c)
+    helpers.parity(C[r, c], ref, dtype, name)
+    plain = helpers.gpu_gemm(layout, dtype, A, B, kernel=hgemm.kernel_index(name[:-len("_persist")]))
+    assert np.array_equal(C, plain), f"{name}: differs from the plain launch"
+
+
 @pytest.mark.parametrize("layout", ["tn", "nn"])
 def test_k_zero_writes_zeros(layout):
     M, N = 40, 48
