@@ -442,7 +442,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
 #pragma unroll
   for (int i = 0; i < NSB; ++i) rb[i] = b_base(i);
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + NSB == tail) mask_tail();  // loads of steps kt+NSB on are issued below
+    if (__builtin_expect(kt + NSB == tail, 0)) mask_tail();  // loads of steps kt+NSB on are issued below
     const uint32_t ca = ra[0], cb = rb[0];
     const uint32_t na = ra[1], nb = rb[1];
     // X: slice 0; read slice 1; A of step kt+NSA-1 into the stage step kt-1 used
