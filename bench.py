@@ -412,7 +412,8 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py: this HGEMM runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(multi-GPU sharding is design-only, see the design notes)", file=sys.stderr)
+              f"(an M or N split across GPUs would need no exchange, but it is not "
+              f"implemented)", file=sys.stderr)
         return 2
 
     import numpy as np

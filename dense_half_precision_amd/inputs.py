@@ -10,7 +10,7 @@ at 512, 2048, 4096 and 8192 and a long-K 8192 x 8192 x 16384 case (the size
 the "MTT S4000 张量核心 GEMM 优化…" post optimises for, section 1).  The pages
 state no value distributions, so uniform and normal draws stand in.
 
-Recipe (also stated in the design notes):
+Recipe:
   * generator: numpy ``Generator(PCG64(seed))``, A seed ``1000 + i``,
     B seed ``2000 + i`` for workload index ``i``;
   * fp16: float64 draws, converted with ``astype(float16)`` (round to nearest
