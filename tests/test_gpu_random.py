@@ -17,7 +17,7 @@ from dense_half_precision_amd import hgemm, inputs
 pytestmark = pytest.mark.gpu
 
 NAN = {"f16": 0x7E00, "bf16": 0x7FC0}
-N_CASES = 48
+N_CASES = 96
 
 
 @pytest.fixture(scope="module", autouse=True)
