@@ -128,6 +128,18 @@ __device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t vo
       r, (__attribute__((address_space(3))) void *)lds_base, 16, voffset, 0, 0, 0);
 }
 
+// load16_lds with the instruction's immediate offset 1024 * J, which moves
+// the LDS destination and the global address alike: four loads into
+// consecutive 1 KiB segments share one lds_base (one M0), each lane's voffset
+// lowered by the immediate.
+template <int J>
+__device__ __forceinline__ void load16_lds_imm(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                               void *lds_base) {
+  static_assert(J >= 0 && J < 4, "immediate offsets 0, 1024, 2048, 3072");
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void *)lds_base, 16, voffset, 0, 1024 * J, 0);
+}
+
 // Workgroup barrier without the memory fence of __syncthreads(): the caller
 // waits (s_waitcnt) for exactly the LDS reads/writes other waves depend on.
 // __syncthreads() would also drain every outstanding direct-to-LDS load

@@ -270,6 +270,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   for (int i = 0; i < SEG_B; ++i)
     b_off[i] = B_MN ? mnmaj_off(wave * SEG_B + i, ldb, 2 * BN, n0, N, b_chunk[i])
                     : kmaj_off(wave * SEG_B + i, ldb, b_chunk[i]);
+  // Loads i and i^1, i^2, i^3 of an operand (four consecutive 1 KiB LDS
+  // segments) share one LDS base address (M0): the immediate offset 1024*(i%4)
+  // moves both the LDS destination and the global address, so each lane's
+  // offset is lowered by it.  The descriptors' base is lowered by kShift
+  // bytes and every offset raised by as much, so that no offset goes below
+  // zero however small the leading dimension; out-of-range offsets stay out
+  // of range.
+  constexpr uint32_t kShift = 4096;
+  auto imm_of = [](int i) { return 1024u * (uint32_t)(i & 3); };
+#pragma unroll
+  for (int i = 0; i < SEG_A; ++i) a_off[i] += kShift - imm_of(i);
+#pragma unroll
+  for (int i = 0; i < SEG_B; ++i) b_off[i] += kShift - imm_of(i);
   const uint16_t *a_panel =
       A_MN ? args.A + m0 + (size_t)k_begin * lda : args.A + (size_t)m0 * lda + k_begin;
   const uint16_t *b_panel =
@@ -293,20 +306,28 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   // branches lose their uniformity and end up in a per-lane loop.)
   auto rsrc_of = [&](bool mn, const uint16_t *panel, int ld, int rows, int k0) {
     const int krem = K - k0;
-    const uint16_t *base = mn ? panel + (size_t)k0 * ld : panel + k0;
+    const char *base = (const char *)(mn ? panel + (size_t)k0 * ld : panel + k0) - kShift;
     const uint32_t bytes = krem <= 0 ? 0u
-                           : mn      ? (uint32_t)(min(krem, BK) * ld) * 2u
-                                     : (uint32_t)((rows - 1) * ld + K - k0) * 2u;
+                           : mn      ? (uint32_t)(min(krem, BK) * ld) * 2u + kShift
+                                     : (uint32_t)((rows - 1) * ld + K - k0) * 2u + kShift;
     return make_rsrc(base, bytes);
   };
   __amdgpu_buffer_rsrc_t rs_a, rs_b;
   auto prep_a = [&](int step) { rs_a = rsrc_of(A_MN, a_panel, lda, rows_a, step * BK); };
   auto prep_b = [&](int step) { rs_b = rsrc_of(B_MN, b_panel, ldb, rows_b, step * BK); };
+  auto load_seg = [&](__amdgpu_buffer_rsrc_t r, uint32_t voff, char *group_base, int i) {
+    switch (i & 3) {
+      case 0: load16_lds_imm<0>(r, voff, group_base); break;
+      case 1: load16_lds_imm<1>(r, voff, group_base); break;
+      case 2: load16_lds_imm<2>(r, voff, group_base); break;
+      default: load16_lds_imm<3>(r, voff, group_base); break;
+    }
+  };
   auto load_a = [&](uint32_t stage, int i) {
-    load16_lds(rs_a, a_off[i], smem + stage + (wave * SEG_A + i) * 1024);
+    load_seg(rs_a, a_off[i], smem + stage + (wave * SEG_A + (i & ~3)) * 1024, i);
   };
   auto load_b = [&](uint32_t stage, int i) {
-    load16_lds(rs_b, b_off[i], smem + stage + (wave * SEG_B + i) * 1024);
+    load_seg(rs_b, b_off[i], smem + stage + (wave * SEG_B + (i & ~3)) * 1024, i);
   };
   // K tail: on the one partial step (K % 64 != 0) a k-chunk past K inside a
   // valid row of a k-contiguous operand would read past the row's end, so from
@@ -321,11 +342,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
     const int kr = K - tail * BK;
     if constexpr (!A_MN) {
 #pragma unroll
-      for (int i = 0; i < SEG_A; ++i) a_off[i] = (a_chunk[i] * 8 < kr) ? a_off[i] : kOutOfRange;
+      for (int i = 0; i < SEG_A; ++i)
+        a_off[i] = (a_chunk[i] * 8 < kr) ? a_off[i] : kOutOfRange + kShift - imm_of(i);
     }
     if constexpr (!B_MN) {
 #pragma unroll
-      for (int i = 0; i < SEG_B; ++i) b_off[i] = (b_chunk[i] * 8 < kr) ? b_off[i] : kOutOfRange;
+      for (int i = 0; i < SEG_B; ++i)
+        b_off[i] = (b_chunk[i] * 8 < kr) ? b_off[i] : kOutOfRange + kShift - imm_of(i);
     }
   };
 
