@@ -270,10 +270,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   for (int i = 0; i < SEG_B; ++i)
     b_off[i] = B_MN ? mnmaj_off(wave * SEG_B + i, ldb, 2 * BN, n0, N, b_chunk[i])
                     : kmaj_off(wave * SEG_B + i, ldb, b_chunk[i]);
-  // Loads i and i^1, i^2, i^3 of an operand (four consecutive 1 KiB LDS
-  // segments) share one LDS base address (M0): the immediate offset 1024*(i%4)
-  // moves both the LDS destination and the global address, so each lane's
-  // offset is lowered by it.  The descriptors' base is lowered by kShift
+  // Loads 4j .. 4j+3 of an operand (four consecutive 1 KiB LDS segments)
+  // share one LDS base address (M0): the immediate offset 1024*(i%4) moves
+  // both the LDS destination and the global address, so each lane's offset
+  // is lowered by it.  The descriptors' base is lowered by kShift
   // bytes and every offset raised by as much, so that no offset goes below
   // zero however small the leading dimension; out-of-range offsets stay out
   // of range.
