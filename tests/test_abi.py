@@ -139,6 +139,10 @@ def test_split_workspace_size_and_validation():
     assert call(4, m=8192, n=8192, k=8192) == uns  # no tail to split
     k128 = hgemm.kernel_index("tn_f16_128x128x64")
     assert call(4, kernel=k128) == uns          # the split runs the 256 x 256 kernels only
+    kp = hgemm.kernel_index("tn_f16_256x256x64_persist")
+    assert call(4, kernel=kp) == uns            # ... that have K-segment launches
+    kws = hgemm.kernel_index("ws_tn_f16_128x256x64")
+    assert call(4, kernel=kws) == uns
 
 
 def test_kernel_table_and_auto_choice():
