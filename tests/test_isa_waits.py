@@ -4,7 +4,7 @@ The NN kernels issue the transposing LDS read as inline assembly that the
 compiler's wait-count pass does not track; these tests prove on the compiled
 code that no instruction uses such a read's destination before a wait that
 covers it, and that no production main loop drains the direct-to-LDS load
-pipeline (vmcnt(0)).  The checker itself is pinned on hand-written assembly
+pipeline (vmcnt(0)).  The wait analysis itself is pinned on hand-written assembly
 with planted mistakes.
 """
 import pytest
@@ -58,7 +58,7 @@ def test_production_loops_keep_loads_in_flight(kernels):
         assert isa_waits.loop_vmcnt_zero(lines) == 0, name
 
 
-# ---------------------------------------------------------------- the checker
+# ---------------------------------------------------------- the wait analysis
 def _k(body):
     return ["k:"] + [("\t" + l if not l.startswith(".") else l) for l in body] + ["\ts_endpgm"]
 
