@@ -205,21 +205,24 @@ def micro() -> int:
               "ms": round(ms, 4), "tflops": round(w.flops / ms / 1e9, 1)})
     # wave specialisation (4 loader + 4 MFMA waves, 128 x 256 tile) against the
     # single-role pipeline on the same tile and the production 256 x 256 kernel,
-    # and the 256 x 256 tile on eight waves (two per SIMD)
+    # and the 256 x 256 tile on eight waves (two per SIMD), both roles in every
+    # wave or two groups alternating memory and MFMA phases
     for (M, N, K) in ((8192, 8192, 8192), (8192, 8192, 16384)):
         A = inputs.draw((M, K), "f16", "uniform", 1)
         Bt = inputs.draw((N, K), "f16", "uniform", 2)
         dA = torch.from_numpy(A.view(np.int16)).cuda()
         dB = torch.from_numpy(Bt.view(np.int16)).cuda()
         dC = torch.empty((M, N), dtype=torch.int16, device="cuda")
-        for name in ("tn_f16_256x256x64", "tn_f16_256x256x64_w2x4", "ws_tn_f16_128x256x64",
-                     "tn_f16_128x256x64"):
+        for name in ("tn_f16_256x256x64", "tn_f16_256x256x64_w2x4", "tn_f16_256x256x64_pp",
+                     "ws_tn_f16_128x256x64", "tn_f16_128x256x64"):
             k = hgemm.kernel_index(name)
             ms = timed(lambda: hgemm.hgemm_tn_ex(M, N, K, "f16", dA.data_ptr(), dB.data_ptr(),
                                                  dC.data_ptr(), sp, kernel=k), n=50, warm=15)
             emit({"micro": "wave_specialisation", "shape": f"{M}x{N}x{K}", "kernel": name,
                   "roles": "4 loader + 4 MFMA waves" if name.startswith("ws_") else
-                  ("8 waves, both roles" if name.endswith("_w2x4") else "4 waves, both roles"),
+                  ("8 waves, both roles" if name.endswith("_w2x4") else
+                   ("8 waves, two groups alternating memory and MFMA phases"
+                    if name.endswith("_pp") else "4 waves, both roles")),
                   "ms": round(ms, 4), "tflops": round(2 * M * N * K / ms / 1e9, 1)})
         del dA, dB, dC
     return 0

@@ -12,6 +12,7 @@
 #include "gemm_kernel.hpp"
 #include "gemm_regstage.hpp"
 #include "gemm_ws_kernel.hpp"
+#include "gemm_pp_kernel.hpp"
 
 namespace {
 
@@ -62,6 +63,13 @@ template <class T, int DT>
 constexpr KernelEntry ws_entry(const char *name, int group_m) {
   return KernelEntry{name, kTN, DT, T::BM, T::BN, T::BK, T::LDS, group_m, false, true,
                      &gemm_ws_kernel<T, DT>, nullptr, nullptr, nullptr, T::NT};
+}
+// two alternating wave groups on the 256 x 256 tile: leading dimensions, alpha
+// and beta, no K split; an ablation, never chosen automatically
+template <int DT>
+constexpr KernelEntry pp_entry(const char *name, int group_m) {
+  return KernelEntry{name, kTN, DT, PpCfg::BM, PpCfg::BN, PpCfg::BK, PpCfg::LDS, group_m, false,
+                     true, &gemm_pp_kernel<DT>, nullptr, nullptr, nullptr, PpCfg::NT};
 }
 // the register-staged baseline assumes packed TN/NN operands, alpha 1, beta 0
 template <class T, int LAYOUT, int DT>
@@ -144,6 +152,10 @@ const KernelEntry kTable[] = {
     persistent_entry<T256, kTN, kF16>("tn_f16_256x256x64_persist", 4, false),
     persistent_entry<T256, kTN, kBF16>("tn_bf16_256x256x64_persist", 4, false),
     persistent_entry<T256, kNN, kBF16>("nn_bf16_256x256x64_persist", 4, false),
+    // the 256 x 256 tile on eight waves in two alternating groups (memory phase /
+    // MFMA phase), TN
+    pp_entry<kF16>("tn_f16_256x256x64_pp", 4),
+    pp_entry<kBF16>("tn_bf16_256x256x64_pp", 4),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 

@@ -120,6 +120,27 @@ def test_persistent_many_tiles(name):
     assert np.array_equal(C, plain), f"{name}: differs from the plain launch"
 
 
+@pytest.mark.parametrize("name", ["tn_f16_256x256x64_pp", "tn_bf16_256x256x64_pp"])
+def test_ping_pong_matches_production_bits(name):
+    """The two-group kernel sums the same 32-k slices in the same order as the
+    production kernel, so the two give the same bits: 3 x 3 tiles with ragged
+    last rows and columns, at K that end on a slice boundary, inside a slice
+    and inside a K step (and shorter than the three-slice load lead), and
+    the oracle on a stratified sample of the largest."""
+    k = hgemm.kernel_table()[hgemm.kernel_index(name)]
+    dtype = "f16" if k["dtype"] == hgemm.F16 else "bf16"
+    prod = hgemm.kernel_index(name[:-len("_pp")])
+    w = inputs.Workload(0, "tn", dtype, 0, 0, 0, "uniform")
+    for s, K in enumerate((8, 40, 96, 1000, 1064)):
+        M, N = 3 * 256 - 37, 3 * 256 - 88
+        A, B = inputs.operands(w, M, N, K, seed_offset=90 + s)
+        C = helpers.gpu_gemm("tn", dtype, A, B, kernel=k["index"])
+        plain = helpers.gpu_gemm("tn", dtype, A, B, kernel=prod)
+        assert np.array_equal(C, plain), f"{name} K={K}: differs from the production kernel"
+    r, c = inputs.stratified_samples(M, N, 95)
+    helpers.parity(C[r, c], oracle.hgemm_sampled("tn", dtype, A, B, r, c), dtype, name)
+
+
 @pytest.mark.parametrize("layout", ["tn", "nn"])
 def test_k_zero_writes_zeros(layout):
     M, N = 40, 48
