@@ -51,6 +51,22 @@ struct PpCfg {
   static_assert(LDS_BYTES <= 163840, "160 KiB of LDS");
 };
 
+// Direct-to-LDS placement of one slice: lane l of 1 KiB segment s (of 16)
+// writes LDS bytes s*1024 + 16*l of the slot, which hold row 16s + l/4,
+// stored chunk l%4, that is logical chunk (l%4) ^ ((row >> 2) & 3).
+__host__ __device__ __forceinline__ void pp_load_place(int s, int lane, int &row, int &chunk) {
+  row = 16 * s + (lane >> 2);
+  chunk = (lane & 3) ^ ((row >> 2) & 3);
+}
+
+// LDS byte offset within a slot that lane l reads for the fragment of rows
+// 16f .. 16f+15: row 16f + l%16, logical chunk l/16 (k = 8*(l/16) .. +7 of
+// the slice), i.e. f*1024 + pp_frag_offset(l).
+__host__ __device__ __forceinline__ uint32_t pp_frag_offset(int lane) {
+  const int row = lane & 15, chunk = lane >> 4;
+  return (uint32_t)(row * 64 + ((chunk ^ ((row >> 2) & 3)) * 16));
+}
+
 template <int DT>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs args) {
   using T = PpCfg;
@@ -72,10 +88,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs args) {
   const int rows_a = min(256, M - m0), rows_b = min(256, N - n0);
   const int NS = (K + 31) / 32;  // slices
 
-  // ---- loads: wave w fills rows 32w .. 32w+31 of each slice of A and of B,
-  // two 1 KiB segments sharing one M0 (immediate offsets 0 and 1024); lane l
-  // of segment s: row 32w + 16s + l/4, stored chunk l%4, so logical chunk
-  // (l%4) ^ ((row >> 2) & 3).  As in the production kernel, the descriptors'
+  // ---- loads: wave w fills segments 2w and 2w+1 (rows 32w .. 32w+31) of
+  // each slice of A and of B, sharing one M0 (immediate offsets 0 and 1024),
+  // placed by pp_load_place.  As in the production kernel, the descriptors'
   // base sits kShift bytes low and every offset kShift bytes high, so that no
   // offset goes below zero; chunks past K get an offset past any range.
   constexpr uint32_t kShift = 4096;
@@ -83,8 +98,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs args) {
   int chunk[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int row = 32 * wave + 16 * s + (lane >> 2);
-    chunk[s] = (lane & 3) ^ ((row >> 2) & 3);
+    int row;
+    pp_load_place(2 * wave + s, lane, row, chunk[s]);
     off_a[s] = (uint32_t)(row * lda + 8 * chunk[s]) * 2u + kShift - 1024u * s;
     off_b[s] = (uint32_t)(row * ldb + 8 * chunk[s]) * 2u + kShift - 1024u * s;
     off_out[s] = kOutOfRange + kShift - 1024u * s;
@@ -116,9 +131,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs args) {
     load16_lds_imm<1>(rb, ob[1], smem + T::B_BASE + slot);
   };
 
-  // ---- fragment reads: tile row 16f + lane%16, logical chunk lane/16 (k =
-  // 8*(lane/16) .. +7 of the slice), the MFMA operand layout
-  const uint32_t rd = (lane & 15) * 64 + (((lane >> 4) ^ ((lane >> 2) & 3)) * 16);
+  // ---- fragment reads (pp_frag_offset): the MFMA operand layout
+  const uint32_t rd = pp_frag_offset(lane);
   const uint32_t rd_a = wm * 128 * 64 + rd;
   const uint32_t rd_b = T::B_BASE + wn * 64 * 64 + rd;
   u32x4 fa[FM], fb[FN];

@@ -9,6 +9,7 @@
 
 #include "hgemm_probe.h"
 #include "gemm_regstage.hpp"
+#include "gemm_pp_kernel.hpp"
 
 namespace {
 
@@ -424,6 +425,15 @@ hgemm_status_t hgemm_probe_operand_offsets(int mn_major, int bx, int *load_row, 
                                  : f * 16 * 128 + (int)kmajor_frag_offset<kLdsXor>(l, sl);
           read_off[((f * 2 + sl) * reads + r) * 64 + l] = o;
         }
+  return HGEMM_OK;
+}
+
+hgemm_status_t hgemm_probe_pp_offsets(int *load_row, int *load_chunk, int *read_off) {
+  if (!load_row || !load_chunk || !read_off) return HGEMM_ERR_INVALID_ARG;
+  for (int seg = 0; seg < 16; ++seg)
+    for (int l = 0; l < 64; ++l) pp_load_place(seg, l, load_row[seg * 64 + l], load_chunk[seg * 64 + l]);
+  for (int f = 0; f < 16; ++f)
+    for (int l = 0; l < 64; ++l) read_off[f * 64 + l] = f * 1024 + (int)pp_frag_offset(l);
   return HGEMM_OK;
 }
 

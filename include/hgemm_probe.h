@@ -78,6 +78,20 @@ hgemm_status_t hgemm_probe_operand_offsets(int mn_major, int bx, int *load_row, 
                                            int *read_off);
 
 /*
+ * Host-side: the LDS placement of one 32-k slice of an operand in the
+ * two-group ("ping-pong") kernel, computed by the functions that kernel uses
+ * (a slot of 256 rows of 64 bytes).
+ *   load_row[s*64 + l], load_chunk[s*64 + l] (16 segments x 64 lanes): the
+ *     row and the logical 16-byte chunk (k = 8*chunk .. +7 of the slice) that
+ *     lane l of direct-to-LDS segment s loads; it lands at LDS byte
+ *     s*1024 + 16*l of the slot.
+ *   read_off[f*64 + l] (16 fragments x 64 lanes): the LDS byte offset lane l
+ *     reads (16 bytes) for the fragment of rows 16f .. 16f+15.
+ * All three are host arrays of 1024 ints.  No GPU work.
+ */
+hgemm_status_t hgemm_probe_pp_offsets(int *load_row, int *load_chunk, int *read_off);
+
+/*
  * LDS layout round trip for a 256-row x 64-column tile of 16-bit values:
  * the tile is written to LDS with the register-staged baseline's store pattern and LDS layout
  * `lds_layout` (0 = XOR swizzle on row/2, 1 = plain rows, 2 = padded rows,

@@ -101,3 +101,25 @@ def test_production_operand_placement(mn_major, bx):
                         o = ro[f, sl, h, 32 * half:32 * half + 32]
                         banks = {(x // 4 + b) % 64 for x in o for b in range(2)}
                         assert len(banks) == 64, (f, sl, h, half)
+
+
+def test_ping_pong_slice_placement():
+    """The two-group kernel's slice layout (the functions the kernel uses, run
+    on the host): every (row, chunk) of a 256-row, 4-chunk slice is loaded
+    exactly once; each fragment read points at row 16f + l%16, chunk l/16,
+    the matrix-core operand; and the 16-lane groups of every read cover the
+    64 banks once."""
+    lr, lc, ro = hgemm.pp_offsets()
+    pairs = list(zip(lr.ravel().tolist(), lc.ravel().tolist()))
+    assert len(set(pairs)) == len(pairs) == 256 * 4
+    assert all(0 <= r < 256 and 0 <= c < 4 for r, c in pairs)
+    loc = {p: 1024 * (i // 64) + 16 * (i % 64) for i, p in enumerate(pairs)}
+    lane = np.arange(64)
+    for f in range(16):
+        want = [loc[(16 * f + l % 16, l // 16)] for l in lane]
+        assert ro[f].tolist() == want, f
+        for q in range(4):
+            o = ro[f, 16 * q:16 * q + 16]
+            banks = {(x // 4 + b) % 64 for x in o for b in range(4)}
+            assert len(banks) == 64, (f, q)
+
