@@ -429,27 +429,27 @@ int layout_of(int opA, int opB) {
 
 extern "C" {
 
-hgemm_status_t hgemm_tn(int64_t M, int64_t N, int64_t K, int dtype, const void *A,
+hgemm_status_t hgemm_tn(int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype, const void *A,
                         const void *Bt, void *C, void *stream) {
   return run(packed(kTN, M, N, K, dtype, A, Bt, C), stream, nullptr);
 }
 
-hgemm_status_t hgemm_nn(int64_t M, int64_t N, int64_t K, int dtype, const void *A,
+hgemm_status_t hgemm_nn(int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype, const void *A,
                         const void *B, void *C, void *stream) {
   return run(packed(kNN, M, N, K, dtype, A, B, C), stream, nullptr);
 }
 
-hgemm_status_t hgemm_tn_ex(int64_t M, int64_t N, int64_t K, int dtype, const void *A,
+hgemm_status_t hgemm_tn_ex(int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype, const void *A,
                            const void *Bt, void *C, void *stream, const hgemm_config_t *cfg) {
   return run(packed(kTN, M, N, K, dtype, A, Bt, C), stream, cfg);
 }
 
-hgemm_status_t hgemm_nn_ex(int64_t M, int64_t N, int64_t K, int dtype, const void *A,
+hgemm_status_t hgemm_nn_ex(int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype, const void *A,
                            const void *B, void *C, void *stream, const hgemm_config_t *cfg) {
   return run(packed(kNN, M, N, K, dtype, A, B, C), stream, cfg);
 }
 
-hgemm_status_t hgemm_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
+hgemm_status_t hgemm_gemm_ex(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype,
                              float alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
                              float beta, void *C, int64_t ldc, void *stream,
                              const hgemm_config_t *cfg) {
@@ -458,21 +458,21 @@ hgemm_status_t hgemm_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, 
   return run(Call{layout, M, N, K, dtype, alpha, beta, A, B, C, lda, ldb, ldc}, stream, cfg);
 }
 
-hgemm_status_t hgemm_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
+hgemm_status_t hgemm_gemm(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype,
                           float alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
                           float beta, void *C, int64_t ldc, void *stream) {
   return hgemm_gemm_ex(opA, opB, M, N, K, dtype, alpha, A, lda, B, ldb, beta, C, ldc, stream,
                        nullptr);
 }
 
-size_t hgemm_gemm_ws_size(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype) {
+size_t hgemm_gemm_ws_size(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype) {
   const int layout = layout_of(opA, opB);
   if (layout < 0 || M <= 0 || N <= 0 || K <= 0 || (dtype != HGEMM_F16 && dtype != HGEMM_BF16))
     return 0;
   return choose(layout, dtype, M, N, K, 0, SIZE_MAX).ws_bytes;
 }
 
-hgemm_status_t hgemm_gemm_ws_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
+hgemm_status_t hgemm_gemm_ws_ex(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype,
                                 float alpha, const void *A, int64_t lda, const void *B,
                                 int64_t ldb, float beta, void *C, int64_t ldc, void *workspace,
                                 size_t ws_bytes, void *stream, const hgemm_config_t *cfg) {
@@ -484,7 +484,7 @@ hgemm_status_t hgemm_gemm_ws_ex(int opA, int opB, int64_t M, int64_t N, int64_t 
   return run(c, stream, cfg);
 }
 
-hgemm_status_t hgemm_gemm_ws(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
+hgemm_status_t hgemm_gemm_ws(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype,
                              float alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
                              float beta, void *C, int64_t ldc, void *workspace, size_t ws_bytes,
                              void *stream) {
@@ -492,8 +492,8 @@ hgemm_status_t hgemm_gemm_ws(int opA, int opB, int64_t M, int64_t N, int64_t K, 
                           workspace, ws_bytes, stream, nullptr);
 }
 
-const char *hgemm_status_string(int status) {
-  switch (status) {
+const char *hgemm_status_string(hgemm_status_t status) {
+  switch ((int)status) {
     case HGEMM_OK: return "ok";
     case HGEMM_ERR_INVALID_ARG: return "invalid argument";
     case HGEMM_ERR_UNSUPPORTED: return "unsupported shape, alignment or config";
@@ -519,7 +519,7 @@ const char *hgemm_kernel_info(int index, int *layout, int *dtype, int *bm, int *
   return e.name;
 }
 
-int hgemm_auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K) {
+int hgemm_auto_kernel(int layout, hgemm_dtype_t dtype, int64_t M, int64_t N, int64_t K) {
   if (layout < kTN || layout > kAtNN || (dtype != HGEMM_F16 && dtype != HGEMM_BF16) || M <= 0 ||
       N <= 0)
     return -1;

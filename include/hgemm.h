@@ -39,7 +39,13 @@
  *
  * Errors: every entry point returns an hgemm_status_t and never prints or
  * throws.  Arguments are validated before anything is launched, so a non-OK
- * status other than HGEMM_ERR_HIP means nothing was enqueued.
+ * status other than HGEMM_ERR_HIP means nothing was enqueued.  The torch
+ * binding of "HGEMM: WMMA 与 MMA PTX 代码学习" (full-listing section) checks
+ * the operands' dtype and shapes before launching and throws a C++ exception
+ * on a mismatch; across a C ABI an exception cannot be caught, so the same
+ * checks return these codes instead (HGEMM_ERR_INVALID_ARG for what that
+ * binding rejects; HGEMM_ERR_UNSUPPORTED for what this library adds:
+ * alignment, N % 8, K % 8 and the size limits).
  */
 #ifndef HGEMM_H
 #define HGEMM_H
@@ -69,12 +75,20 @@ typedef enum hgemm_status {
                                 hgemm_last_hip_error() */
 } hgemm_status_t;
 
-/* C[M,N] = A[M,K] * Bt[N,K]^T.  A, Bt, C as described above. */
-hgemm_status_t hgemm_tn(int64_t M, int64_t N, int64_t K, int dtype,
+typedef enum hgemm_op {
+  HGEMM_OP_N = 0, /* operand used as stored */
+  HGEMM_OP_T = 1  /* operand stored transposed */
+} hgemm_op_t;
+
+/* C[M,N] = A[M,K] * Bt[N,K]^T.  A, Bt, C as described above.  (The pages'
+ * "TN": the B operand is read as stored N x K, as the kernel of the HGEMM MMA
+ * note, full-listing section, reads it.) */
+hgemm_status_t hgemm_tn(int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype,
                         const void *A, const void *Bt, void *C, void *stream);
 
-/* C[M,N] = A[M,K] * B[K,N].  A, B, C as described above. */
-hgemm_status_t hgemm_nn(int64_t M, int64_t N, int64_t K, int dtype,
+/* C[M,N] = A[M,K] * B[K,N].  A, B, C as described above.  (The pages' "NN":
+ * A, B and C all row-major, the HGEMM MMA note's kernel header.) */
+hgemm_status_t hgemm_nn(int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype,
                         const void *A, const void *B, void *C, void *stream);
 
 /*
@@ -102,17 +116,13 @@ hgemm_status_t hgemm_nn(int64_t M, int64_t N, int64_t K, int dtype,
  * operand (OP_N A, OP_T B) and 2^23 for an M/N-contiguous one, ldc below 2^31
  * (else HGEMM_ERR_UNSUPPORTED).  With beta != 0, C must not overlap A or B.
  */
-typedef enum hgemm_op {
-  HGEMM_OP_N = 0, /* operand used as stored */
-  HGEMM_OP_T = 1  /* operand stored transposed */
-} hgemm_op_t;
-
-hgemm_status_t hgemm_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
-                          float alpha, const void *A, int64_t lda, const void *B,
-                          int64_t ldb, float beta, void *C, int64_t ldc, void *stream);
+hgemm_status_t hgemm_gemm(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N, int64_t K,
+                          hgemm_dtype_t dtype, float alpha, const void *A, int64_t lda,
+                          const void *B, int64_t ldb, float beta, void *C, int64_t ldc,
+                          void *stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
-const char *hgemm_status_string(int status);
+const char *hgemm_status_string(hgemm_status_t status);
 
 /* hipError_t of this thread's last HGEMM_ERR_HIP (0 if none yet). */
 int hgemm_last_hip_error(void);
@@ -125,7 +135,11 @@ const char *hgemm_version(void);
  * design choice with counters (tile shape, LDS layout, block-index swizzle).
  * The pages' launchers expose the same kind of knobs at run time (stages,
  * block swizzle on/off and its stride) in the torch bindings of the HGEMM
- * MMA note and the CuTe note.
+ * MMA note and the CuTe note.  Here the tile, the LDS stage ring and the LDS
+ * layout (XOR swizzle, unswizzled, padded rows) are compile-time properties of
+ * a kernel, so they are chosen together by a kernel-table index, whose name
+ * (hgemm_kernel_info) states them; the block-index swizzle is chosen at run
+ * time by group_m and xcd_remap.
  */
 typedef struct hgemm_config {
   int32_t kernel;    /* index into the kernel table, or -1 for the automatic
@@ -142,10 +156,10 @@ typedef struct hgemm_config {
 } hgemm_config_t;
 
 /* As hgemm_tn / hgemm_nn, with an explicit configuration (NULL = automatic). */
-hgemm_status_t hgemm_tn_ex(int64_t M, int64_t N, int64_t K, int dtype,
+hgemm_status_t hgemm_tn_ex(int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype,
                            const void *A, const void *Bt, void *C, void *stream,
                            const hgemm_config_t *cfg);
-hgemm_status_t hgemm_nn_ex(int64_t M, int64_t N, int64_t K, int dtype,
+hgemm_status_t hgemm_nn_ex(int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype,
                            const void *A, const void *B, void *C, void *stream,
                            const hgemm_config_t *cfg);
 /*
@@ -174,24 +188,25 @@ hgemm_status_t hgemm_nn_ex(int64_t M, int64_t N, int64_t K, int dtype,
  * NULL) the call runs unsplit.
  * workspace: device memory, 16-byte aligned, owned by the caller.
  */
-size_t hgemm_gemm_ws_size(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype);
+size_t hgemm_gemm_ws_size(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N, int64_t K,
+                          hgemm_dtype_t dtype);
 
-hgemm_status_t hgemm_gemm_ws(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
-                             float alpha, const void *A, int64_t lda, const void *B,
+hgemm_status_t hgemm_gemm_ws(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N, int64_t K,
+                             hgemm_dtype_t dtype, float alpha, const void *A, int64_t lda, const void *B,
                              int64_t ldb, float beta, void *C, int64_t ldc, void *workspace,
                              size_t ws_bytes, void *stream);
 
 /* As hgemm_gemm_ws, with an explicit configuration (NULL = automatic);
  * cfg->split > 0 forces that split (HGEMM_ERR_UNSUPPORTED when there is no
  * tail, S exceeds the K steps, or the workspace is too small). */
-hgemm_status_t hgemm_gemm_ws_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, int dtype,
-                                float alpha, const void *A, int64_t lda, const void *B,
+hgemm_status_t hgemm_gemm_ws_ex(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N,
+                                int64_t K, hgemm_dtype_t dtype, float alpha, const void *A, int64_t lda, const void *B,
                                 int64_t ldb, float beta, void *C, int64_t ldc, void *workspace,
                                 size_t ws_bytes, void *stream, const hgemm_config_t *cfg);
 
 /* As hgemm_gemm, with an explicit configuration (NULL = automatic). */
-hgemm_status_t hgemm_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K,
-                             int dtype, float alpha, const void *A, int64_t lda,
+hgemm_status_t hgemm_gemm_ex(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N, int64_t K,
+                             hgemm_dtype_t dtype, float alpha, const void *A, int64_t lda,
                              const void *B, int64_t ldb, float beta, void *C,
                              int64_t ldc, void *stream, const hgemm_config_t *cfg);
 
@@ -200,8 +215,9 @@ int hgemm_kernel_count(void);
 
 /* Description of kernel table entry `index` (NULL if out of range):
  * "<layout>_<dtype>_<BM>x<BN>x<BK>" for the production kernels (the ones the
- * automatic choice uses: entries 0..11 and 20..31; "at_" layouts take A
- * stored transposed), with a suffix naming what an
+ * automatic choice uses: entries 0..11, 20..31 and the deeper-ring "_r3"
+ * entries 38..45, see hgemm_auto_kernel; "at_" layouts take A stored
+ * transposed), with a suffix naming what an
  * ablation changes ("_plainlds": LDS without the XOR swizzle, "_directepi":
  * epilogue without LDS staging), and an "rs_" prefix for the register-staged
  * 32x32x16 baseline design (suffix: its LDS layout).  The integers describing
@@ -222,7 +238,7 @@ const char *hgemm_kernel_info(int index, int *layout, int *dtype, int *bm,
  * entry with one more LDS stage per operand (the "_r3" names).  This is the
  * choice of hgemm_tn, hgemm_nn and hgemm_gemm; hgemm_gemm_ws may split K
  * instead. */
-int hgemm_auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K);
+int hgemm_auto_kernel(int layout, hgemm_dtype_t dtype, int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus
 }

@@ -60,10 +60,6 @@ def _load(mutation: int = 0) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     i64, u16p, f64p, i64p = (ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16),
                              ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64))
-    lib.oracle_decode.argtypes = [ctypes.c_int, ctypes.c_uint16]
-    lib.oracle_decode.restype = ctypes.c_double
-    lib.oracle_round.argtypes = [ctypes.c_int, ctypes.c_double]
-    lib.oracle_round.restype = ctypes.c_uint16
     lib.oracle_decode_array.argtypes = [ctypes.c_int, u16p, f64p, i64]
     lib.oracle_round_array.argtypes = [ctypes.c_int, f64p, u16p, i64]
     lib.oracle_hgemm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, u16p, u16p, u16p]
@@ -74,8 +70,6 @@ def _load(mutation: int = 0) -> ctypes.CDLL:
     lib.oracle_hgemm_sampled.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, u16p, u16p,
                                          i64p, i64p, i64, u16p]
     lib.oracle_hgemm_sampled.restype = ctypes.c_int
-    lib.oracle_hgemm_f64.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, u16p, u16p, f64p]
-    lib.oracle_hgemm_f64.restype = ctypes.c_int
     dbl = ctypes.c_double
     lib.oracle_gemm_rows.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64, dbl,
                                      u16p, i64, u16p, i64, dbl, u16p, i64, u16p, i64, i64, i64]
@@ -171,20 +165,6 @@ def hgemm_sampled(layout, dtype, A: np.ndarray, B: np.ndarray, rows: np.ndarray,
     if rc != 0:
         raise RuntimeError(f"oracle_hgemm_sampled failed with {rc}")
     return out
-
-
-def hgemm_f64(layout, dtype, A: np.ndarray, B: np.ndarray, mutation: int = 0) -> np.ndarray:
-    """Unrounded FP64 sums (float64, shape [M, N])."""
-    lay = _code(_LAYOUTS, layout)
-    A, B = _u16(A), _u16(B)
-    M, N, K = _shapes(lay, A, B)
-    C = np.empty((M, N), dtype=np.float64)
-    rc = _load(mutation).oracle_hgemm_f64(lay, _code(_DTYPES, dtype), M, N, K,
-                                          _ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16),
-                                          _ptr(C, ctypes.c_double))
-    if rc != 0:
-        raise RuntimeError(f"oracle_hgemm_f64 failed with {rc}")
-    return C
 
 
 # ------------------------------------------------------------------ general form

@@ -153,17 +153,8 @@ static uint16_t encode16(double v, const fmt_t *f) {
 }
 
 /* ---------------------------------------------------------------------- */
-/* Exported scalar/array helpers (used by the oracle's own pins).          */
+/* Exported array helpers (checked exhaustively by the oracle's own pins). */
 /* ---------------------------------------------------------------------- */
-double oracle_decode(int dtype, uint16_t bits) {
-  return decode16(bits, fmt_of(dtype));
-}
-
-uint16_t oracle_round(int dtype, double x) {
-  const fmt_t *f = fmt_of(dtype);
-  return encode16(round_to_format(x, f), f);
-}
-
 void oracle_decode_array(int dtype, const uint16_t *in, double *out,
                          int64_t n) {
   const fmt_t *f = fmt_of(dtype);
@@ -271,23 +262,14 @@ int oracle_hgemm_sampled(int layout, int dtype, int64_t M, int64_t N,
   const fmt_t *f = fmt_of(dtype);
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t i = 0; i < count; ++i) {
+#if ORACLE_MUTATION == 12
+    /* planted mistake: row and column of the sample swapped */
+    const double s = dot(layout, lut, A, B, N, K, cols[i], rows[i]);
+#else
     const double s = dot(layout, lut, A, B, N, K, rows[i], cols[i]);
+#endif
     out[i] = encode16(round_to_format(s, f), f);
   }
-  free(lut);
-  return 0;
-}
-
-/* The unrounded FP64 sums, for the error-bound pins.  */
-int oracle_hgemm_f64(int layout, int dtype, int64_t M, int64_t N, int64_t K,
-                     const uint16_t *A, const uint16_t *B, double *C) {
-  if (check_args(layout, dtype, M, N, K)) return -1;
-  double *lut = make_lut(dtype);
-  if (!lut) return -2;
-#pragma omp parallel for schedule(dynamic, 1)
-  for (int64_t m = 0; m < M; ++m)
-    for (int64_t n = 0; n < N; ++n)
-      C[m * N + n] = dot(layout, lut, A, B, N, K, m, n);
   free(lut);
   return 0;
 }
@@ -401,8 +383,18 @@ int oracle_gemm_sampled(int opA, int opB, int dtype, int64_t M, int64_t N,
   const fmt_t *f = fmt_of(dtype);
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t i = 0; i < count; ++i) {
+#if ORACLE_MUTATION == 10
+    /* planted mistake: row and column of the sample swapped */
+    const double v = gen_element(opA, opB, lut, N, K, alpha, A, lda, B, ldb,
+                                 beta, Cin, ldcin, cols[i], rows[i]);
+#elif ORACLE_MUTATION == 11
+    /* planted mistake: the old C read with the packed stride N, not ldcin */
+    const double v = gen_element(opA, opB, lut, N, K, alpha, A, lda, B, ldb,
+                                 beta, Cin, N, rows[i], cols[i]);
+#else
     const double v = gen_element(opA, opB, lut, N, K, alpha, A, lda, B, ldb,
                                  beta, Cin, ldcin, rows[i], cols[i]);
+#endif
     out[i] = encode16(round_to_format(v, f), f);
   }
   free(lut);

@@ -56,6 +56,12 @@ def freivalds(C_bits: np.ndarray, A_bits: np.ndarray, B_bits: np.ndarray, layout
     M, N = C_bits.shape
     x = g.choice(np.array([-1.0, 1.0]), size=N)
     C = decode(C_bits, dtype)
+    # An unwritten element keeps the NaN fill of the output buffer; a NaN
+    # would also make the tolerance below NaN and every comparison pass, so
+    # non-finite output fails here first.
+    nonfinite = np.argwhere(~np.isfinite(C))
+    assert nonfinite.size == 0, (f"Freivalds check: {len(nonfinite)} non-finite output "
+                                 f"elements, first at {tuple(nonfinite[0])}")
     Bv = decode(B_bits, dtype)
     y = Bv.T @ x if layout == "tn" else Bv @ x  # Bop x, length K
     del Bv

@@ -331,15 +331,31 @@ def pin_gemm_layout_invariants(mutation: int = 0):
         same_bits(tn.T, oracle.hgemm("tn", dt, Bt, A, mutation=mutation), f"transpose {dt}")
 
 
+def _all_pairs(M: int, N: int, seed: int):
+    """Every (row, column) of an M x N output, in a seeded random order."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    idx = g.permutation(M * N)
+    return idx // N, idx % N
+
+
 def pin_gemm_sampled_matches_full(mutation: int = 0):
-    """The sampled entry point returns the same bits as the full one."""
-    M, N, K = 37, 45, 64
-    A = inputs.draw((M, K), "f16", "uniform", 41)
-    Bt = inputs.draw((N, K), "f16", "uniform", 42)
-    full = oracle.hgemm("tn", "f16", A, Bt, mutation=mutation)
-    r, c = inputs.stratified_samples(M, N, 5, bands=8)
-    same_bits(oracle.hgemm_sampled("tn", "f16", A, Bt, r, c, mutation=mutation), full[r, c],
-              "sampled vs full")
+    """The sampled entry point returns the same bits as the full one, at
+    every element (in a shuffled order) and at stratified samples, both
+    layouts and dtypes.  The first shape is square, so that a build that swaps
+    a sample's row and column still reads inside the operands and fails on
+    the first comparison."""
+    for s, (M, N, K) in enumerate(((40, 40, 24), (37, 45, 64), (45, 37, 40))):
+        for dt in ("f16", "bf16"):
+            for layout in ("tn", "nn"):
+                A = inputs.draw((M, K), dt, "uniform", 41 + s)
+                B = inputs.draw((N, K) if layout == "tn" else (K, N), dt, "uniform", 42 + s)
+                full = oracle.hgemm(layout, dt, A, B, mutation=mutation)
+                r, c = _all_pairs(M, N, 43 + s)
+                same_bits(oracle.hgemm_sampled(layout, dt, A, B, r, c, mutation=mutation),
+                          full[r, c], f"sampled vs full, every element, {dt} {layout} {M}x{N}")
+                r, c = inputs.stratified_samples(M, N, 5, bands=8)
+                same_bits(oracle.hgemm_sampled(layout, dt, A, B, r, c, mutation=mutation),
+                          full[r, c], f"sampled vs full, stratified, {dt} {layout} {M}x{N}")
 
 
 def pin_golden(mutation: int = 0):
@@ -463,11 +479,47 @@ def pin_general_matches_layouts(mutation: int = 0):
                   oracle.hgemm("nn", dt, A, Bn, mutation=mutation), f"general vs nn {dt}")
 
 
+GENERAL_SAMPLED_CASES = [  # (M, N, K, alpha, beta); the first is square
+    (40, 40, 24, 1.5, -0.5), (37, 45, 64, -0.75, 0.25), (45, 37, 17, 2.0, 0.0),
+    (29, 51, 9, 1.0, 0.0),
+]
+
+
+def pin_general_sampled_matches_full(mutation: int = 0):
+    """The general form's sampled entry point returns the same bits as its
+    full one (itself pinned to exact rational arithmetic above), at every
+    element in a shuffled order: all four operation-flag pairs, padded
+    leading dimensions (the old C's too), dyadic alpha/beta, and an old C
+    filled with NaN when beta == 0.  The first case is square, so that a
+    build that swaps a sample's row and column still reads inside the
+    operands and fails on the first comparison."""
+    for s, (M, N, K, al, be) in enumerate(GENERAL_SAMPLED_CASES):
+        for dt in ("f16", "bf16"):
+            for opA in (0, 1):
+                for opB in (0, 1):
+                    A = inputs.draw((M, K), dt, "normal", 600 + s)
+                    Bl = inputs.draw((K, N), dt, "normal", 700 + s)
+                    As = _stored(A, opA == 1, 8 + s % 3, 0x3C00)
+                    Bs = _stored(Bl, opB == 1, 3 + s % 2, 0x3C00)
+                    if be != 0:
+                        Cs = _stored(inputs.draw((M, N), dt, "normal", 800 + s), False, 5, 0x3C00)
+                    else:
+                        Cs = np.full((M, N + 5), _NAN_BITS[dt], dtype=np.uint16)
+                    full = oracle.gemm(opA, opB, dt, M, N, K, As, Bs, al, be, Cs,
+                                       mutation=mutation)
+                    r, c = _all_pairs(M, N, 900 + s)
+                    got = oracle.gemm_sampled(opA, opB, dt, M, N, K, As, Bs, r, c, al, be, Cs,
+                                              mutation=mutation)
+                    same_bits(got, full[r, c],
+                              f"general sampled vs full {dt} op{opA}{opB} {M}x{N}x{K} "
+                              f"a={al} b={be}")
+
+
 ALL_PINS = [
     pin_decode_exhaustive, pin_round_representable, pin_round_midpoints, pin_round_random,
     pin_round_special, pin_gemm_bruteforce, pin_gemm_small_integers,
     pin_gemm_identity_permutation, pin_gemm_closed_forms, pin_gemm_ties,
     pin_gemm_layout_invariants, pin_gemm_sampled_matches_full, pin_golden,
     pin_general_bruteforce, pin_general_small_integers, pin_general_padding_and_beta_zero,
-    pin_general_matches_layouts,
+    pin_general_matches_layouts, pin_general_sampled_matches_full,
 ]

@@ -216,6 +216,10 @@ def test_determinism_and_streams():
     first = helpers.gpu_gemm("nn", "bf16", A, B, dA=dA, dB=dB)
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     outs = [helpers.empty_dev(2048, 2048) for _ in range(4)]
+    # the NaN fills above run on the current stream: the two side streams wait
+    # for them before the GEMMs overwrite the outputs
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
     for i, o in enumerate(outs):
         s = s1 if i % 2 == 0 else s2
         st = hgemm.hgemm_nn(2048, 2048, 1024, "bf16", dA.data_ptr(), dB.data_ptr(), o.data_ptr(),

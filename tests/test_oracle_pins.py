@@ -17,8 +17,10 @@ def test_oracle_pin(pin):
 
 # Each planted mistake (a dropped k term, B read with the wrong layout, ties
 # rounded away from zero, truncation, a wrong bfloat16 exponent bias, a sign
-# error, and in the general form: beta ignored, a transposed A read as
-# stored, B's leading dimension ignored) must make at least one pin fail.
+# error; in the general form: beta ignored, a transposed A read as stored, B's
+# leading dimension ignored; in the sampled entry points: a sample's row and
+# column swapped, the old C's leading dimension ignored) must make at least
+# one pin fail.
 MUTATIONS = {
     1: "last k term dropped",
     2: "NN operand read as TN",
@@ -29,6 +31,9 @@ MUTATIONS = {
     7: "general form ignores beta",
     8: "general form reads a transposed A as stored",
     9: "general form ignores the leading dimension of B",
+    10: "general sampled form swaps a sample's row and column",
+    11: "general sampled form ignores the leading dimension of the old C",
+    12: "sampled TN/NN form swaps a sample's row and column",
 }
 
 
