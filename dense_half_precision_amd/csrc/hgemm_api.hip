@@ -7,6 +7,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "hgemm.h"
 #include "gemm_kernel.hpp"
@@ -411,6 +412,52 @@ hgemm_status_t run(const Call &c, void *stream, const hgemm_config_t *cfg) {
   return launch(e.fixup, a.grid, a, stream, kFixupThreads);
 }
 
+// ---- the no-allocation variant of hgemm_gemm_ws ----------------------------
+// The K split's FP32 partial sums go to this file-scope array instead of a
+// caller workspace.  Each device that runs the library holds its own copy,
+// kNoAllocScratchBytes, from the code object's load until the process ends.
+// Its device address differs per device and is not the host-side name's
+// address: it is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that pointer is handed to kernels.  No kernel
+// expects it to start at zero (every partial sum is written before the fixup
+// reads it), so calls never clear it; calls that overlap in time on one device
+// share it and race.
+constexpr size_t kNoAllocScratchBytes = HGEMM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+static_assert(kNoAllocScratchBytes % 256 == 0, "whole 256 KiB slots");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call there); nullptr with the status in *st on failure.
+void *scratch_on_current_device(hgemm_status_t *st) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    *st = HGEMM_ERR_HIP;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *st = HGEMM_ERR_UNSUPPORTED;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || p == nullptr) {
+      g_last_hip_error = (int)(err != hipSuccess ? err : hipErrorInvalidSymbol);
+      *st = HGEMM_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // The pages' two layouts: packed storage, alpha 1, beta 0.
 Call packed(int layout, int64_t M, int64_t N, int64_t K, int dtype, const void *A, const void *B,
             void *C) {
@@ -492,12 +539,35 @@ hgemm_status_t hgemm_gemm_ws(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t 
                           workspace, ws_bytes, stream, nullptr);
 }
 
+hgemm_status_t hgemm_gemm_noalloc(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N,
+                                  int64_t K, hgemm_dtype_t dtype, float alpha, const void *A,
+                                  int64_t lda, const void *B, int64_t ldb, float beta, void *C,
+                                  int64_t ldc, void *stream) {
+  const int layout = layout_of(opA, opB);
+  if (layout < 0) return HGEMM_ERR_INVALID_ARG;
+  Call c{layout, M, N, K, dtype, alpha, beta, A, B, C, lda, ldb, ldc};
+  hgemm_status_t st = validate(c);
+  if (st != HGEMM_OK || c.M == 0 || c.N == 0) return st;
+  // the plan hgemm_gemm_ws would take with an unlimited workspace
+  const size_t need = choose(layout, dtype, M, N, K, 0, SIZE_MAX).ws_bytes;
+  if (need > kNoAllocScratchBytes) return HGEMM_ERR_SCRATCH;
+  if (need > 0) {
+    c.ws = scratch_on_current_device(&st);
+    if (c.ws == nullptr) return st;
+    c.ws_bytes = kNoAllocScratchBytes;
+  }
+  return run(c, stream, nullptr);
+}
+
 const char *hgemm_status_string(hgemm_status_t status) {
   switch ((int)status) {
     case HGEMM_OK: return "ok";
     case HGEMM_ERR_INVALID_ARG: return "invalid argument";
     case HGEMM_ERR_UNSUPPORTED: return "unsupported shape, alignment or config";
     case HGEMM_ERR_HIP: return "HIP runtime error";
+    case HGEMM_ERR_SCRATCH:
+      return "the K split would need more than the library's static scratch "
+             "(HGEMM_NOALLOC_SCRATCH_BYTES); call hgemm_gemm_ws with a workspace";
     default: return "unknown status";
   }
 }

@@ -18,7 +18,8 @@ HEADERS = [os.path.join(ROOT, "include", h) for h in ("hgemm.h", "hgemm_probe.h"
 F16, BF16 = 0, 1
 TN, NN, AT_TN, AT_NN = 0, 1, 2, 3  # kernel layouts (hgemm_kernel_info)
 OP_N, OP_T = 0, 1                  # operation flags of hgemm_gemm
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_SCRATCH = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 64 << 20  # HGEMM_NOALLOC_SCRATCH_BYTES
 DTYPE_CODES = {"f16": F16, "fp16": F16, "float16": F16, "bf16": BF16, "bfloat16": BF16}
 LDS_XOR, LDS_PLAIN, LDS_PAD, LDS_XOR_ROW = 0, 1, 2, 3
 
@@ -75,6 +76,8 @@ def _lib() -> ctypes.CDLL:
     lib.hgemm_gemm_ws.restype = i32
     lib.hgemm_gemm_ws_ex.argtypes = ws + [ctypes.POINTER(Config)]
     lib.hgemm_gemm_ws_ex.restype = i32
+    lib.hgemm_gemm_noalloc.argtypes = general
+    lib.hgemm_gemm_noalloc.restype = i32
     lib.hgemm_gemm_ws_size.argtypes = [i32, i32, i64, i64, i64, i32]
     lib.hgemm_gemm_ws_size.restype = ctypes.c_size_t
     lib.hgemm_status_string.argtypes = [i32]
@@ -178,6 +181,14 @@ def hgemm_gemm_ws(opA, opB, M, N, K, dtype, alpha, A, lda, B, ldb, beta, C, ldc,
         return _lib().hgemm_gemm_ws(*args)
     cfg = Config(-1 if kernel is None else kernel, group_m, xcd_remap, split)
     return _lib().hgemm_gemm_ws_ex(*args, ctypes.byref(cfg))
+
+
+def hgemm_gemm_noalloc(opA, opB, M, N, K, dtype, alpha, A, lda, B, ldb, beta, C, ldc,
+                       stream=0) -> int:
+    """General form with the K split's partial sums in the library's static
+    scratch: no allocation, no workspace (see include/hgemm.h)."""
+    return _lib().hgemm_gemm_noalloc(opA, opB, M, N, K, _dt(dtype), float(alpha), A, lda, B, ldb,
+                                     float(beta), C, ldc, stream)
 
 
 def gemm_ws_size(opA, opB, M, N, K, dtype) -> int:

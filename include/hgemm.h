@@ -70,9 +70,11 @@ typedef enum hgemm_status {
   HGEMM_ERR_UNSUPPORTED = 2, /* N or K not a multiple of 8, a pointer not
                                 16-byte aligned, a dimension over the limits
                                 above, or a config that does not fit */
-  HGEMM_ERR_HIP = 3          /* the HIP runtime refused a launch; the
+  HGEMM_ERR_HIP = 3,         /* the HIP runtime refused a launch; the
                                 hipError_t is kept per thread, see
                                 hgemm_last_hip_error() */
+  HGEMM_ERR_SCRATCH = 4      /* hgemm_gemm_noalloc: the call needs more than
+                                the library's static scratch */
 } hgemm_status_t;
 
 typedef enum hgemm_op {
@@ -203,6 +205,30 @@ hgemm_status_t hgemm_gemm_ws_ex(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64
                                 int64_t K, hgemm_dtype_t dtype, float alpha, const void *A, int64_t lda, const void *B,
                                 int64_t ldb, float beta, void *C, int64_t ldc, void *workspace,
                                 size_t ws_bytes, void *stream, const hgemm_config_t *cfg);
+
+/*
+ * No-allocation variant of hgemm_gemm_ws, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, result
+ * and kernels as hgemm_gemm_ws with a large enough workspace (bit-identical
+ * output), but the K split's partial sums go to a static device array of the
+ * library, HGEMM_NOALLOC_SCRATCH_BYTES (64 MiB) on each device it runs on,
+ * held from the library's first use there until the process ends.  The call
+ * allocates nothing.
+ *   - Calls whose automatic split needs more (hgemm_gemm_ws_size above the
+ *     limit) return HGEMM_ERR_SCRATCH and enqueue nothing.
+ *   - The array is shared by every call on a device and keeps the last
+ *     call's contents: calls that overlap in time on one device (concurrent
+ *     streams, threads) race and give wrong results; order them.
+ *   - The first call on a device looks up the array's device address
+ *     (HGEMM_ERR_HIP if the runtime refuses), with that device current: the
+ *     stream must belong to the current device.
+ */
+#define HGEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hgemm_status_t hgemm_gemm_noalloc(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N,
+                                  int64_t K, hgemm_dtype_t dtype, float alpha, const void *A,
+                                  int64_t lda, const void *B, int64_t ldb, float beta, void *C,
+                                  int64_t ldc, void *stream);
 
 /* As hgemm_gemm, with an explicit configuration (NULL = automatic). */
 hgemm_status_t hgemm_gemm_ex(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N, int64_t K,

@@ -145,6 +145,35 @@ def test_split_workspace_size_and_validation():
     assert call(4, kernel=kws) == uns
 
 
+def test_noalloc_refusals_on_the_host():
+    """hgemm_gemm_noalloc validates like hgemm_gemm and refuses, before any
+    HIP call, a shape whose automatic K split needs more partial-sum bytes
+    than the library's static scratch holds."""
+    f = hgemm.lib().hgemm_gemm_noalloc
+    lim = hgemm.NOALLOC_SCRATCH_BYTES
+    size = hgemm.gemm_ws_size
+
+    def call(m, n, k, opA=0, opB=1, dt=0, lda=None, ldb=None, ldc=None, ptr=FAKE):
+        lda = lda if lda is not None else (m if opA else k)
+        ldb = ldb if ldb is not None else (k if opB else n)
+        return f(opA, opB, m, n, k, dt, 1.0, ptr, lda, ptr, ldb, 0.0, ptr,
+                 ldc if ldc is not None else n, 0)
+    assert hgemm.lib().hgemm_status_string(hgemm.ERR_SCRATCH).decode().startswith("the K split")
+    # over the limit: 7680^2 x 7680 has a tail of 132 tiles; 4608^2 x 8192 68
+    over = [(m, n, k) for (m, n, k) in ((7680, 7680, 7680), (4608, 4608, 8192), (3328, 3328, 16384))
+            if size(0, 1, m, n, k, "f16") > lim]
+    assert over, "no shape over the scratch limit among the candidates"
+    for m, n, k in over:
+        assert call(m, n, k) == hgemm.ERR_SCRATCH
+    assert size(0, 1, 6144, 6144, 6144, "f16") == lim  # exactly the limit: accepted (GPU test)
+    assert call(-1, 8, 8) == hgemm.ERR_INVALID_ARG
+    assert call(8, 8, 8, opA=2) == hgemm.ERR_INVALID_ARG
+    assert call(8, 8, 8, dt=7) == hgemm.ERR_INVALID_ARG
+    assert call(8, 12, 8) == hgemm.ERR_UNSUPPORTED       # N % 8
+    assert call(8, 8, 8, ptr=FAKE + 2) == hgemm.ERR_UNSUPPORTED
+    assert call(0, 8, 8) == hgemm.OK                      # empty: nothing to do
+
+
 def test_kernel_table_and_auto_choice():
     tab = hgemm.kernel_table()
     assert len(tab) == hgemm.lib().hgemm_kernel_count() > 0
