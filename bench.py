@@ -24,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2516.6  # MI355X dense FP16/BF16 matrix peak: 256 CU x 4096 FLOP/clk x 2.4 GHz
+CU_FLOP_PER_CLK = 256 * 4096  # the same peak per engine clock (the clock-adjusted peak's slope)
 HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_hgemm_tn_f16_8192.json")
 # the benched kernel's device code (the traffic figures stay valid while it is unchanged;
@@ -369,6 +370,106 @@ def tail() -> int:
     return 0
 
 
+def engine_clock_mhz(w, dA, dB, dC, kname: str, launches: int):
+    """Engine clock the kernel runs at, from its measurement copy (the "_clk"
+    twin of the same kernel, which writes the shader clock and the 100 MHz
+    real-time clock at the start and end of every workgroup): total shader
+    cycles over total real time of all workgroups of `launches` back-to-back
+    launches on the launch stream.  None if the kernel has no such twin."""
+    import numpy as np
+    import torch
+    from dense_half_precision_amd import hgemm
+    try:
+        k = hgemm.kernel_index(kname + "_clk")
+    except KeyError:
+        return None
+    info = hgemm.kernel_table()[k]
+    tiles = -(-w.M // info["bm"]) * -(-w.N // info["bn"])
+    ts = torch.zeros((launches, tiles, 4), dtype=torch.int64, device="cuda")
+    opB = hgemm.OP_T if w.layout == "tn" else hgemm.OP_N
+    ldb = w.K if w.layout == "tn" else w.N
+    sp = torch.cuda.current_stream().cuda_stream
+    for i in range(launches):
+        st = hgemm.hgemm_gemm_ws(hgemm.OP_N, opB, w.M, w.N, w.K, w.dtype, 1.0, dA.data_ptr(), w.K,
+                                 dB.data_ptr(), ldb, 0.0, dC.data_ptr(), w.N,
+                                 ts[i].data_ptr(), tiles * 32, sp, kernel=k)
+        if st != hgemm.OK:
+            raise hgemm.HgemmError(st, "clock measurement launch")
+    torch.cuda.synchronize()
+    t = ts.cpu().numpy().astype(np.float64)
+    cycles = (t[..., 2] - t[..., 0]).sum()
+    real = (t[..., 3] - t[..., 1]).sum()
+    return float(cycles / real * 100.0) if real > 0 else None
+
+
+def time_workload(w, dA, dB, dC, steps: int, warmup: int):
+    """HIP events on the launch stream around each of `steps` launches of the
+    automatic choice (after `warmup`); returns (kernel name, per-launch ms)."""
+    import numpy as np
+    import torch
+    from dense_half_precision_amd import hgemm
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    fn = hgemm.lib().hgemm_tn if w.layout == "tn" else hgemm.lib().hgemm_nn
+    args = (w.M, w.N, w.K, hgemm.F16 if w.dtype == "f16" else hgemm.BF16, dA.data_ptr(),
+            dB.data_ptr(), dC.data_ptr(), sp)
+    for _ in range(warmup):
+        fn(*args)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        st = fn(*args)
+        b.record(stream)
+        if st != hgemm.OK:
+            raise hgemm.HgemmError(st, "workload launch")
+    torch.cuda.synchronize()
+    kname = hgemm.kernel_table()[hgemm.auto_kernel(
+        hgemm.TN if w.layout == "tn" else hgemm.NN, w.dtype, w.M, w.N, w.K)]["name"]
+    return kname, np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def workload_line(w, kname, per_ms, mhz):
+    import numpy as np
+    med = float(np.median(per_ms))
+    tf = w.flops / (med * 1e-3) / 1e12
+    line = {"workload": w.name, "kernel": kname, "launches": int(len(per_ms)),
+            "kernel_us_median": round(med * 1e3, 2), "kernel_us_min": round(float(per_ms.min()) * 1e3, 2),
+            "tflops": round(tf, 1), "frac": round(tf / PEAK_TFLOPS, 4),
+            "sclk_mhz": round(mhz) if mhz else None,
+            "clock_adjusted_frac": round(tf / (CU_FLOP_PER_CLK * mhz * 1e-6), 4) if mhz else None}
+    return line
+
+
+def all_workloads(headline_index: int, headline_line: dict, cpu_threads: int):
+    """Every workload (1..5): kernel-event median over its launches, TFLOPS,
+    fraction of the nameplate peak, engine clock and the fraction of the peak
+    at that clock.  The headline workload's line is the one already measured."""
+    import numpy as np
+    import torch
+    from dense_half_precision_amd import inputs
+    lines = []
+    for w in inputs.WORKLOADS:
+        if w.index == headline_index:
+            lines.append(headline_line)
+            continue
+        A, B = inputs.operands(w)
+        dA = torch.from_numpy(A.view(np.int16)).cuda()
+        dB = torch.from_numpy(B.view(np.int16)).cuda()
+        dC = torch.empty((w.M, w.N), dtype=torch.int16, device="cuda")
+        del A, B
+        small = w.flops < 1e11
+        kname, per = time_workload(w, dA, dB, dC, steps=200 if small else 30,
+                                   warmup=50 if small else 10)
+        mhz = engine_clock_mhz(w, dA, dB, dC, kname, launches=200 if small else 30)
+        lines.append(workload_line(w, kname, per, mhz))
+        print(f"[bench] {w.name}: {lines[-1]}", file=sys.stderr, flush=True)
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+    return lines
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -394,6 +495,9 @@ def main() -> int:
                          "time and back to back")
     ap.add_argument("--oracle-table", action="store_true",
                     help="time the CPU oracle on every workload (host only) and exit")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="leave out the per-workload list (all five workloads timed after "
+                         "the headline run)")
     args = ap.parse_args()
     if args.oracle_table:
         return oracle_table(args.workload if "--workload" in sys.argv else 0)
@@ -500,6 +604,11 @@ def main() -> int:
     print(f"[bench] kernel ms: mean {k_avg:.4f} median {np.median(per):.4f} min {per.min():.4f} "
           f"max {per.max():.4f}; wall ms/step {ms_step:.4f}", file=sys.stderr, flush=True)
 
+    # engine clock of the same kernel on the same operands, right after the
+    # timed region (its measurement copy; outside the timed region)
+    mhz = engine_clock_mhz(w, dA, dB, dC, kname, launches=args.steps)
+    print(f"[bench] engine clock {mhz:.0f} MHz" if mhz else "[bench] engine clock n/a",
+          file=sys.stderr, flush=True)
     tb = traffic_bytes(kname)
     out = {
         "metric": "HGEMM TFLOPS and % of MI355X dense FP16/BF16 MFMA peak at 4096³/8192³",
@@ -523,8 +632,16 @@ def main() -> int:
                      "kernel_ms": {"mean": round(k_avg, 5), "median": round(float(np.median(per)), 5),
                                    "min": round(float(per.min()), 5), "max": round(float(per.max()), 5)},
                      "algorithmic_flops_per_launch": w.flops,
-                     "algorithmic_bytes_per_launch": w.algorithmic_bytes},
+                     "algorithmic_bytes_per_launch": w.algorithmic_bytes,
+                     "sclk_mhz": round(mhz) if mhz else None,
+                     "clock_adjusted_peak": round(CU_FLOP_PER_CLK * mhz * 1e-6, 1) if mhz else None,
+                     "clock_adjusted_frac": (round(achieved / (CU_FLOP_PER_CLK * mhz * 1e-6), 4)
+                                             if mhz else None)},
     }
+    if not args.no_workloads:
+        out["workloads"] = all_workloads(w.index, workload_line(w, kname, per, mhz),
+                                         int(os.environ.get("OMP_NUM_THREADS",
+                                                            os.cpu_count() or 1)))
     if args.cpu_seconds > 0:
         print(f"[bench] cpu_baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
               flush=True)

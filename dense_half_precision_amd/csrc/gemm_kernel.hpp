@@ -569,7 +569,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
 //     positions b, b + gridDim.x, ... of `grid`: the same tile on the same XCD
 //     in the same round as kWhole, but the next tile's loads start while the
 //     last one's stores of C drain, and no workgroup is launched per tile.
-enum LaunchMode { kWhole = 0, kSegments = 1, kMixed = 2, kPersistent = 3 };
+//   kTimed: kWhole, and workgroup b writes four 64-bit counters to
+//     ((uint64_t *)ws)[4b ..]: the shader clock (s_memtime) and the 100 MHz
+//     real-time clock (s_memrealtime) before its tile and after its stores
+//     of C are issued.  Their ratio is the engine clock the tiles ran at (a
+//     measurement copy: the power limit of the part sets that clock).
+enum LaunchMode { kWhole = 0, kSegments = 1, kMixed = 2, kPersistent = 3, kTimed = 4 };
 
 template <class T, int LAYOUT, int DT, int MODE>
 __global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs args) {
@@ -578,6 +583,18 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs args) {
   if constexpr (MODE == kWhole) {
     const int p = __builtin_amdgcn_readfirstlane(xcd_position(b, args.grid, args.xcd_remap));
     gemm_tile<T, LAYOUT, DT, false>(args, smem, args.tile_begin + p, 0, 0);
+  } else if constexpr (MODE == kTimed) {
+    const uint64_t c0 = clock64(), r0 = wall_clock64();
+    const int p = __builtin_amdgcn_readfirstlane(xcd_position(b, args.grid, args.xcd_remap));
+    gemm_tile<T, LAYOUT, DT, false>(args, smem, args.tile_begin + p, 0, 0);
+    const uint64_t c1 = clock64(), r1 = wall_clock64();
+    if (threadIdx.x == 0) {
+      uint64_t *t = reinterpret_cast<uint64_t *>(args.ws) + 4 * (size_t)b;
+      t[0] = c0;
+      t[1] = r0;
+      t[2] = c1;
+      t[3] = r1;
+    }
   } else if constexpr (MODE == kPersistent) {
     for (int v = b; v < args.grid; v += gridDim.x) {
       const int p = __builtin_amdgcn_readfirstlane(xcd_position(v, args.grid, args.xcd_remap));

@@ -35,6 +35,7 @@ struct KernelEntry {
   int threads = 256;   // workgroup size of fn, split_fn and mixed_fn
   int nsb = 2;         // B stages of the LDS ring (A has one more)
   bool persistent = false;  // fn runs one workgroup per CU over all tiles
+  bool timed = false;       // fn writes per-workgroup clock counters to the workspace
 };
 constexpr int kFixupThreads = 256;  // gemm_sk_fixup's workgroup size
 
@@ -50,6 +51,15 @@ constexpr KernelEntry persistent_entry(const char *name, int group_m, bool produ
   return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, production, true,
                      &gemm_kernel<T, LAYOUT, DT, kPersistent>, nullptr, nullptr, nullptr, T::NT,
                      T::NSB, true};
+}
+// the production kernel with per-workgroup clock counters (launch mode
+// kTimed): measures the engine clock a shape runs at; never chosen
+// automatically
+template <class T, int LAYOUT, int DT>
+constexpr KernelEntry timed_entry(const char *name, int group_m) {
+  return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, false, true,
+                     &gemm_kernel<T, LAYOUT, DT, kTimed>, nullptr, nullptr, nullptr, T::NT,
+                     T::NSB, false, true};
 }
 // whole-K tiles only (no K-split instantiations)
 template <class T, int LAYOUT, int DT>
@@ -157,6 +167,11 @@ const KernelEntry kTable[] = {
     // MFMA phase), TN
     pp_entry<kF16>("tn_f16_256x256x64_pp", 4),
     pp_entry<kBF16>("tn_bf16_256x256x64_pp", 4),
+    // production kernels with per-workgroup clock counters (measurement copies)
+    timed_entry<T256, kTN, kF16>("tn_f16_256x256x64_clk", 4),
+    timed_entry<T256, kNN, kBF16>("nn_bf16_256x256x64_clk", 4),
+    timed_entry<T128R3, kTN, kF16>("tn_f16_128x128x64_r3_clk", 4),
+    timed_entry<T64, kTN, kF16>("tn_f16_64x64x64_clk", 4),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -390,6 +405,10 @@ hgemm_status_t run(const Call &c, void *stream, const hgemm_config_t *cfg) {
   a.sk_split = 0;
   a.sk_tiles = 0;
   a.ws = nullptr;
+  if (e.timed) {  // 32 bytes of clock counters per workgroup in the workspace
+    if (c.ws == nullptr || c.ws_bytes < (size_t)tiles * 32) return HGEMM_ERR_UNSUPPORTED;
+    a.ws = static_cast<float *>(c.ws);
+  }
   if (plan.split == 0)
     return launch(e.fn, e.persistent ? std::min<int64_t>(tiles, kCUs) : tiles, a, stream,
                   e.threads);

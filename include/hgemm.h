@@ -200,7 +200,11 @@ hgemm_status_t hgemm_gemm_ws(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t 
 
 /* As hgemm_gemm_ws, with an explicit configuration (NULL = automatic);
  * cfg->split > 0 forces that split (HGEMM_ERR_UNSUPPORTED when there is no
- * tail, S exceeds the K steps, or the workspace is too small). */
+ * tail, S exceeds the K steps, or the workspace is too small).  A "_clk"
+ * kernel (a measurement copy of a production kernel) writes four uint64_t
+ * per workgroup b to the workspace at index 4b: shader clock and 100 MHz
+ * real-time clock before the tile, then both after its stores of C are
+ * issued; it needs 32 bytes per workgroup (HGEMM_ERR_UNSUPPORTED otherwise). */
 hgemm_status_t hgemm_gemm_ws_ex(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N,
                                 int64_t K, hgemm_dtype_t dtype, float alpha, const void *A, int64_t lda, const void *B,
                                 int64_t ldb, float beta, void *C, int64_t ldc, void *workspace,
@@ -246,7 +250,9 @@ int hgemm_kernel_count(void);
  * transposed), with a suffix naming what an
  * ablation changes ("_plainlds": LDS without the XOR swizzle, "_directepi":
  * epilogue without LDS staging), and an "rs_" prefix for the register-staged
- * 32x32x16 baseline design (suffix: its LDS layout).  The integers describing
+ * 32x32x16 baseline design (suffix: its LDS layout), and a "_clk" suffix for
+ * measurement copies that record per-workgroup clocks (see hgemm_gemm_ws_ex).
+ * The integers describing
  * it are written through the non-NULL pointers: layout 0 = TN (A[M][K],
  * Bt[N][K]), 1 = NN (A[M][K], B[K][N]), 2 = at_tn (At[K][M], Bt[N][K]), 3 =
  * at_nn (At[K][M], B[K][N]); dtype
