@@ -7,9 +7,18 @@ output): the configuration whose throughput is quoted as a fraction of the
 MI355X dense FP16 matrix peak.  Inputs are seeded synthetic data, resident
 in HBM before the timed region starts.
 
+Before the warmup steps the workload runs back to back for --settle-ms
+(300 ms by default): when load starts after idle, the part's power
+controller first pulls the engine clock far below the level it settles at,
+and recovers over tens of milliseconds (`--clock-trace` measures this); the
+settle phase keeps that transient out of the timed region and is reported in
+the JSON line.
+
 Prints one JSON line with TFLOPS (2*M*N*K / time), the roofline position of
-the kernel (HIP-event timing of every launch on the launch stream) and the
-CPU oracle's throughput on a bounded sample of the same workload.
+the kernel (HIP-event timing of every launch on the launch stream, the engine
+clock from the kernel's measurement copy and the fraction of the peak at
+that clock), the same figures for all five workloads, and the CPU oracle's
+throughput on a bounded sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -229,6 +238,51 @@ def micro() -> int:
     return 0
 
 
+def mix() -> int:
+    """What memory instructions cost the matrix cores of the wave that issues
+    them (one JSON line per case): hgemm_probe_mix with 64 MFMAs per
+    iteration and 0..16 loads of each kind (1 KiB straight into LDS; 1 KiB
+    into registers then written to LDS; 256 bytes straight into LDS), with
+    and without 16 LDS fragment reads; cycles per MFMA (16 at full rate) and
+    the extra cycles per load over the case without loads."""
+    import numpy as np
+    import torch
+    from dense_half_precision_amd import hgemm
+    lib = hgemm.lib()
+    sp = torch.cuda.current_stream().cuda_stream
+    wgs, iters, window = 256, 2000, 4 << 20
+    buf = torch.zeros(window // 2, dtype=torch.int16, device="cuda")
+    out = torch.empty(wgs * 256, device="cuda")
+    clk = torch.zeros(2 * 4 * wgs, dtype=torch.int64, device="cuda")
+    kinds = {0: "1 KiB direct-to-LDS", 1: "1 KiB into registers, then ds_write", 2: "256 B direct-to-LDS"}
+    base = {}
+    cases = [(nread, kind, nload) for nread in (0, 16) for kind in (0, 1, 2)
+             for nload in (0, 2, 4, 8, 16)]
+    cases += [(256 + nread, 0, nload) for nread in (0, 16) for nload in (0, 8, 16)]
+    for nread, kind, nload in cases:
+        if True:
+            if True:
+                for rep in range(3):  # the first launch warms the window into L2
+                    st = lib.hgemm_probe_mix(kind, nload, nread, wgs, iters, buf.data_ptr(), window,
+                                             out.data_ptr(), clk.data_ptr(), sp)
+                    if st != hgemm.OK:
+                        raise hgemm.HgemmError(st, "mix probe")
+                torch.cuda.synchronize()
+                c = clk.cpu().numpy().reshape(-1, 2).astype(np.float64)
+                cyc = float(np.median(c[:, 0])) / (64.0 * iters)
+                mhz = float(np.median(c[:, 0] / c[:, 1]) * 100.0)
+                if nload == 0:
+                    base[nread] = cyc
+                line = {"micro": "mfma_load_mix", "load": kinds[kind], "loads_per_64_mfma": nload,
+                        "lds_reads_per_64_mfma": nread % 256, "barrier_per_128_mfma": nread >= 256,
+                        "cycles_per_mfma": round(cyc, 3),
+                        "mfma_busy": round(16.0 / cyc, 4), "sclk_mhz": round(mhz)}
+                if nload > 0:
+                    line["extra_cycles_per_load"] = round((cyc - base[nread]) * 64.0 / nload, 2)
+                print(json.dumps(line), flush=True)
+    return 0
+
+
 def compare() -> int:
     """This library's automatic choice against torch.mm (the vendor library) on
     the five workloads, one JSON line each, measured two ways: one launch at a
@@ -370,41 +424,81 @@ def tail() -> int:
     return 0
 
 
-def engine_clock_mhz(w, dA, dB, dC, kname: str, launches: int):
-    """Engine clock the kernel runs at, from its measurement copy (the "_clk"
+class EngineClock:
+    """Engine clock a kernel runs at, from its measurement copy (the "_clk"
     twin of the same kernel, which writes the shader clock and the 100 MHz
     real-time clock at the start and end of every workgroup): total shader
-    cycles over total real time of all workgroups of `launches` back-to-back
-    launches on the launch stream.  None if the kernel has no such twin."""
-    import numpy as np
+    cycles over total real time of all workgroups of `launches` launches.
+
+    The counter buffer is allocated up front; enqueue() adds the launches to
+    the stream without waiting, so that they follow the preceding launches
+    with no idle gap (a gap of a few milliseconds is enough for the power
+    controller to pull the clock down again); mhz() reads the result after
+    the caller has synchronised.  Unavailable (None) if the kernel has no
+    measurement copy."""
+
+    def __init__(self, w, dA, dB, dC, kname: str, launches: int):
+        import torch
+        from dense_half_precision_amd import hgemm
+        self.k = None
+        try:
+            self.k = hgemm.kernel_index(kname + "_clk")
+        except KeyError:
+            return
+        info = hgemm.kernel_table()[self.k]
+        self.tiles = -(-w.M // info["bm"]) * -(-w.N // info["bn"])
+        self.ts = torch.zeros((launches, self.tiles, 4), dtype=torch.int64, device="cuda")
+        opB = hgemm.OP_T if w.layout == "tn" else hgemm.OP_N
+        ldb = w.K if w.layout == "tn" else w.N
+        self.args = (hgemm.OP_N, opB, w.M, w.N, w.K, w.dtype, 1.0, dA.data_ptr(), w.K,
+                     dB.data_ptr(), ldb, 0.0, dC.data_ptr(), w.N)
+        self.launches = launches
+
+    def enqueue(self):
+        import torch
+        from dense_half_precision_amd import hgemm
+        if self.k is None:
+            return
+        sp = torch.cuda.current_stream().cuda_stream
+        for i in range(self.launches):
+            st = hgemm.hgemm_gemm_ws(*self.args, self.ts[i].data_ptr(), self.tiles * 32, sp,
+                                     kernel=self.k)
+            if st != hgemm.OK:
+                raise hgemm.HgemmError(st, "clock measurement launch")
+
+    def mhz(self):
+        import numpy as np
+        if self.k is None:
+            return None
+        t = self.ts.cpu().numpy().astype(np.float64)
+        cycles = (t[..., 2] - t[..., 0]).sum()
+        real = (t[..., 3] - t[..., 1]).sum()
+        return float(cycles / real * 100.0) if real > 0 else None
+
+
+def settle(launch, settle_ms: float):
+    """Launch back to back, in batches of up to 10 launches with a wait after
+    each batch, until `settle_ms` of wall time have passed.  When load starts
+    after idle, the power controller first pulls the engine clock well below
+    where it settles (measured: `bench.py --clock-trace`); this keeps that
+    transient out of the timed region.  Returns (launches, ms)."""
     import torch
-    from dense_half_precision_amd import hgemm
-    try:
-        k = hgemm.kernel_index(kname + "_clk")
-    except KeyError:
-        return None
-    info = hgemm.kernel_table()[k]
-    tiles = -(-w.M // info["bm"]) * -(-w.N // info["bn"])
-    ts = torch.zeros((launches, tiles, 4), dtype=torch.int64, device="cuda")
-    opB = hgemm.OP_T if w.layout == "tn" else hgemm.OP_N
-    ldb = w.K if w.layout == "tn" else w.N
-    sp = torch.cuda.current_stream().cuda_stream
-    for i in range(launches):
-        st = hgemm.hgemm_gemm_ws(hgemm.OP_N, opB, w.M, w.N, w.K, w.dtype, 1.0, dA.data_ptr(), w.K,
-                                 dB.data_ptr(), ldb, 0.0, dC.data_ptr(), w.N,
-                                 ts[i].data_ptr(), tiles * 32, sp, kernel=k)
-        if st != hgemm.OK:
-            raise hgemm.HgemmError(st, "clock measurement launch")
-    torch.cuda.synchronize()
-    t = ts.cpu().numpy().astype(np.float64)
-    cycles = (t[..., 2] - t[..., 0]).sum()
-    real = (t[..., 3] - t[..., 1]).sum()
-    return float(cycles / real * 100.0) if real > 0 else None
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(10):
+            launch()
+            n += 1
+        torch.cuda.synchronize()
+    return n, round((time.perf_counter() - t0) * 1e3, 1)
 
 
-def time_workload(w, dA, dB, dC, steps: int, warmup: int):
-    """HIP events on the launch stream around each of `steps` launches of the
-    automatic choice (after `warmup`); returns (kernel name, per-launch ms)."""
+def time_workload(w, dA, dB, dC, steps: int, warmup: int, settle_ms: float = 0.0):
+    """The automatic choice on one workload: settle, the engine clock
+    (measurement copy, enqueued with no gap), `warmup` launches, then `steps`
+    launches with HIP events on the launch stream around each, then `steps`
+    launches back to back without events (wall clock between
+    synchronisations).  Returns (kernel name, per-launch ms, back-to-back ms
+    per launch, MHz)."""
     import numpy as np
     import torch
     from dense_half_precision_amd import hgemm
@@ -413,11 +507,17 @@ def time_workload(w, dA, dB, dC, steps: int, warmup: int):
     fn = hgemm.lib().hgemm_tn if w.layout == "tn" else hgemm.lib().hgemm_nn
     args = (w.M, w.N, w.K, hgemm.F16 if w.dtype == "f16" else hgemm.BF16, dA.data_ptr(),
             dB.data_ptr(), dC.data_ptr(), sp)
+    kname = hgemm.kernel_table()[hgemm.auto_kernel(
+        hgemm.TN if w.layout == "tn" else hgemm.NN, w.dtype, w.M, w.N, w.K)]["name"]
+    clk = EngineClock(w, dA, dB, dC, kname, launches=steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    if settle_ms > 0:
+        settle(lambda: fn(*args), settle_ms)
+    clk.enqueue()
     for _ in range(warmup):
         fn(*args)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     for a, b in ev:
         a.record(stream)
         st = fn(*args)
@@ -425,12 +525,15 @@ def time_workload(w, dA, dB, dC, steps: int, warmup: int):
         if st != hgemm.OK:
             raise hgemm.HgemmError(st, "workload launch")
     torch.cuda.synchronize()
-    kname = hgemm.kernel_table()[hgemm.auto_kernel(
-        hgemm.TN if w.layout == "tn" else hgemm.NN, w.dtype, w.M, w.N, w.K)]["name"]
-    return kname, np.array([a.elapsed_time(b) for a, b in ev])
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn(*args)
+    torch.cuda.synchronize()
+    b2b = (time.perf_counter() - t0) * 1e3 / steps
+    return kname, np.array([a.elapsed_time(b) for a, b in ev]), b2b, clk.mhz()
 
 
-def workload_line(w, kname, per_ms, mhz):
+def workload_line(w, kname, per_ms, mhz, b2b_ms=None):
     import numpy as np
     med = float(np.median(per_ms))
     tf = w.flops / (med * 1e-3) / 1e12
@@ -439,10 +542,13 @@ def workload_line(w, kname, per_ms, mhz):
             "tflops": round(tf, 1), "frac": round(tf / PEAK_TFLOPS, 4),
             "sclk_mhz": round(mhz) if mhz else None,
             "clock_adjusted_frac": round(tf / (CU_FLOP_PER_CLK * mhz * 1e-6), 4) if mhz else None}
+    if b2b_ms is not None:
+        line["back_to_back_us"] = round(b2b_ms * 1e3, 2)
+        line["back_to_back_tflops"] = round(w.flops / (b2b_ms * 1e-3) / 1e12, 1)
     return line
 
 
-def all_workloads(headline_index: int, headline_line: dict, cpu_threads: int):
+def all_workloads(headline_index: int, headline_line: dict, settle_ms: float):
     """Every workload (1..5): kernel-event median over its launches, TFLOPS,
     fraction of the nameplate peak, engine clock and the fraction of the peak
     at that clock.  The headline workload's line is the one already measured."""
@@ -460,14 +566,61 @@ def all_workloads(headline_index: int, headline_line: dict, cpu_threads: int):
         dC = torch.empty((w.M, w.N), dtype=torch.int16, device="cuda")
         del A, B
         small = w.flops < 1e11
-        kname, per = time_workload(w, dA, dB, dC, steps=200 if small else 30,
-                                   warmup=50 if small else 10)
-        mhz = engine_clock_mhz(w, dA, dB, dC, kname, launches=200 if small else 30)
-        lines.append(workload_line(w, kname, per, mhz))
+        kname, per, b2b, mhz = time_workload(w, dA, dB, dC, steps=200 if small else 30,
+                                             warmup=50 if small else 10, settle_ms=settle_ms)
+        lines.append(workload_line(w, kname, per, mhz, b2b))
         print(f"[bench] {w.name}: {lines[-1]}", file=sys.stderr, flush=True)
         del dA, dB, dC
         torch.cuda.empty_cache()
     return lines
+
+
+def clock_trace(widx: int, launches: int, idle_s: float = 2.0) -> int:
+    """The engine clock over a run of back-to-back launches that starts after
+    `idle_s` of GPU idle time: the measurement copy of the workload's kernel
+    ("_clk" twin) records per-workgroup shader and real-time clocks, and each
+    window of 10 launches prints its start time, median duration, clock and
+    TFLOPS (one JSON line per window).  Shows how long the power controller
+    takes to settle after load starts."""
+    import numpy as np
+    import torch
+    from dense_half_precision_amd import hgemm, inputs
+    w = inputs.workload(widx)
+    A, B = inputs.operands(w)
+    dA = torch.from_numpy(A.view(np.int16)).cuda()
+    dB = torch.from_numpy(B.view(np.int16)).cuda()
+    dC = torch.empty((w.M, w.N), dtype=torch.int16, device="cuda")
+    kname = hgemm.kernel_table()[hgemm.auto_kernel(
+        hgemm.TN if w.layout == "tn" else hgemm.NN, w.dtype, w.M, w.N, w.K)]["name"]
+    k = hgemm.kernel_index(kname + "_clk")
+    info = hgemm.kernel_table()[k]
+    tiles = -(-w.M // info["bm"]) * -(-w.N // info["bn"])
+    ts = torch.zeros((launches, tiles, 4), dtype=torch.int64, device="cuda")
+    opB = hgemm.OP_T if w.layout == "tn" else hgemm.OP_N
+    ldb = w.K if w.layout == "tn" else w.N
+    sp = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    time.sleep(idle_s)
+    for i in range(launches):
+        st = hgemm.hgemm_gemm_ws(hgemm.OP_N, opB, w.M, w.N, w.K, w.dtype, 1.0, dA.data_ptr(), w.K,
+                                 dB.data_ptr(), ldb, 0.0, dC.data_ptr(), w.N,
+                                 ts[i].data_ptr(), tiles * 32, sp, kernel=k)
+        if st != hgemm.OK:
+            raise hgemm.HgemmError(st, "clock trace launch")
+    torch.cuda.synchronize()
+    t = ts.cpu().numpy().astype(np.float64)
+    r_first = t[..., 1].min()
+    win = 10
+    for j in range(0, launches, win):
+        seg = t[j:j + win]
+        dur = (seg[..., 3].max(axis=1) - seg[..., 1].min(axis=1)) / 100.0  # us
+        mhz = [((x[:, 2] - x[:, 0]).sum() / (x[:, 3] - x[:, 1]).sum() * 100.0) for x in seg]
+        print(json.dumps({"clock_trace": w.name, "kernel": kname, "launches": [j, j + len(seg) - 1],
+                          "start_ms": round((seg[..., 1].min() - r_first) / 1e5, 3),
+                          "dur_us_median": round(float(np.median(dur)), 2),
+                          "sclk_mhz": round(float(np.median(mhz))),
+                          "tflops": round(w.flops / float(np.median(dur)) / 1e6, 1)}), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -486,6 +639,8 @@ def main() -> int:
                          "(reference point for scaling FETCH_SIZE/WRITE_SIZE counters)")
     ap.add_argument("--micro", action="store_true",
                     help="run the microbenchmarks behind the design choices and exit")
+    ap.add_argument("--mix", action="store_true",
+                    help="matrix-core rate with loads and LDS reads mixed in (hgemm_probe_mix)")
     ap.add_argument("--tail", action="store_true",
                     help="K split of the tail vs the unsplit choice and torch.mm, per shape")
     ap.add_argument("--vendor", action="store_true",
@@ -495,6 +650,13 @@ def main() -> int:
                          "time and back to back")
     ap.add_argument("--oracle-table", action="store_true",
                     help="time the CPU oracle on every workload (host only) and exit")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="before the warmup steps, launch the workload back to back for this "
+                         "long, so that the engine clock has left the power controller's "
+                         "start-of-load dip (0: no settling)")
+    ap.add_argument("--clock-trace", type=int, default=0, metavar="LAUNCHES",
+                    help="print the engine clock over this many back-to-back launches of the "
+                         "workload's kernel after 2 s idle, and exit")
     ap.add_argument("--no-workloads", action="store_true",
                     help="leave out the per-workload list (all five workloads timed after "
                          "the headline run)")
@@ -506,6 +668,16 @@ def main() -> int:
             print("bench.py: one GPU only", file=sys.stderr)
             return 2
         return tail()
+    if args.clock_trace > 0:
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            return 2
+        return clock_trace(args.workload, args.clock_trace)
+    if args.mix:
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            return 2
+        return mix()
     if args.micro:
         if args.gpus != 1:
             print("bench.py: one GPU only", file=sys.stderr)
@@ -581,9 +753,17 @@ def main() -> int:
 
     print(f"[bench] {w.describe()}; kernel {kname}; warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
+    # engine clock: the kernel's measurement copy, enqueued between the settle
+    # phase and the warmup steps with no gap (outside the timed region)
+    clk = EngineClock(w, dA, dB, dC, kname, launches=max(args.steps, 10))
+    settled = settle(launch, args.settle_ms) if args.settle_ms > 0 else (0, 0.0)
+    print(f"[bench] clock settle: {settled[0]} launches in {settled[1]} ms", file=sys.stderr,
+          flush=True)
+    clk.enqueue()
     for _ in range(args.warmup):
         launch()
     torch.cuda.synchronize()
+    mhz = clk.mhz()
 
     # timed region: events on the launch stream around every launch
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -604,9 +784,6 @@ def main() -> int:
     print(f"[bench] kernel ms: mean {k_avg:.4f} median {np.median(per):.4f} min {per.min():.4f} "
           f"max {per.max():.4f}; wall ms/step {ms_step:.4f}", file=sys.stderr, flush=True)
 
-    # engine clock of the same kernel on the same operands, right after the
-    # timed region (its measurement copy; outside the timed region)
-    mhz = engine_clock_mhz(w, dA, dB, dC, kname, launches=args.steps)
     print(f"[bench] engine clock {mhz:.0f} MHz" if mhz else "[bench] engine clock n/a",
           file=sys.stderr, flush=True)
     tb = traffic_bytes(kname)
@@ -625,7 +802,10 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "layout": w.layout, "M": w.M, "N": w.N, "K": w.K,
                    "inputs": w.describe(), "kernel": kname, "accumulate": "fp32",
-                   "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2)},
+                   "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+                   "clock_settle": {"launches": settled[0], "ms": settled[1],
+                                    "note": "back-to-back launches before the warmup steps, "
+                                            "outside the timed region"}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": tb,
@@ -640,8 +820,7 @@ def main() -> int:
     }
     if not args.no_workloads:
         out["workloads"] = all_workloads(w.index, workload_line(w, kname, per, mhz),
-                                         int(os.environ.get("OMP_NUM_THREADS",
-                                                            os.cpu_count() or 1)))
+                                         args.settle_ms)
     if args.cpu_seconds > 0:
         print(f"[bench] cpu_baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
               flush=True)

@@ -254,6 +254,143 @@ __global__ __launch_bounds__(256) void probe_mfma_rate_kernel(int iters, float *
   }
 }
 
+// Matrix-core issue rate with memory instructions mixed in, one wave per SIMD
+// (four per workgroup, one workgroup per CU): each iteration issues 64
+// 16x16x32 MFMAs (random FP16 operands, 16 independent accumulators) and,
+// spread evenly among them,
+//   NLOAD loads of kind KIND out of an L2-resident window:
+//     0: buffer_load_dwordx4 ... lds (1 KiB into LDS per instruction; four
+//        loads share one LDS base through the immediate offset),
+//     1: buffer_load_dwordx4 into registers (1 KiB per instruction), written
+//        to LDS with ds_write_b128 in the second half of the iteration,
+//     2: buffer_load_dword ... lds (256 bytes into LDS per instruction);
+//   NREAD 16-byte LDS reads (ds_read_b128) of a region no load writes.
+// Kinds 0 and 2 wait at the end of an iteration only for the previous
+// iteration's loads; reads are consumed at the end of their iteration.
+// clocks[2w], clocks[2w+1]: shader clock cycles and real-time ticks of wave w
+// over the loop; cycles / (64 * iters) is the time per MFMA (16 at full rate).
+template <int KIND, int NLOAD, int NREAD, bool BAR = false>
+__global__ __launch_bounds__(256) void probe_mix_kernel(const uint16_t *buf, uint32_t window,
+                                                        int iters, float *out, uint64_t *clocks) {
+  __shared__ __attribute__((aligned(1024))) char smem[65536];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  u32x4 x[8], y[8];
+  uint32_t h = 0x9E3779B9u * (uint32_t)(t + 1);
+  for (int i = 0; i < 8; ++i)
+    for (int e = 0; e < 4; ++e) {
+      h = h * 1664525u + 1013904223u;
+      const uint32_t w = (h & 0x83FF83FFu) | 0x38003800u;
+      x[i][e] = w;
+      y[i][e] = (w ^ 0x80008000u) + (uint32_t)i;
+    }
+  f32x4 acc[16];
+  for (int j = 0; j < 16; ++j) acc[j] = f32x4{};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) asm volatile("" : "+a"(acc[j]));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(x[i]), "+v"(y[i]));
+  // LDS: wave w owns [16w KiB, 16w+16 KiB): loads land in its first 8 KiB,
+  // reads come from its last 8 KiB
+  for (int i = t; i < 65536 / 16; i += 256) ((u32x4 *)smem)[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  char *dst = smem + wave * 16384;
+  const uint32_t rd = (uint32_t)(wave * 16384 + 8192 + lane * 16);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(buf, window);
+  const uint32_t mask = window - 1;  // a power of two
+  uint32_t base = ((blockIdx.x * 4u + (uint32_t)wave) * 16384u) & mask;
+  constexpr int LSP = (KIND == 1 ? 32 : 64) / (NLOAD > 0 ? NLOAD : 64);  // MFMAs per load
+  constexpr int RSP = 64 / (NREAD > 0 ? NREAD : 64);                     // MFMAs per read
+  u32x4 gv[KIND == 1 && NLOAD > 0 ? NLOAD : 1];
+  u32x4 rv[NREAD > 0 ? NREAD : 1];
+  asm volatile("s_nop 7" ::: "memory");
+  const uint64_t c0 = clock64(), r0 = wall_clock64();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      if constexpr (BAR) {
+        // a workgroup barrier every 128 MFMAs, in the middle of every other
+        // iteration, after the waits a pipelined GEMM step has there
+        if (j == 32 && (it & 1)) {
+          __builtin_amdgcn_s_waitcnt(waitcnt_imm(KIND == 1 ? 0 : NLOAD, 0));
+          wg_barrier();
+        }
+      }
+      mfma_pinned<1>(acc[j & 15], x[j & 7], y[(j >> 3) & 7]);
+      if constexpr (NLOAD > 0) {
+        if (j % LSP == 0 && j / LSP < NLOAD) {
+          const int i = j / LSP;
+          const uint32_t so = (base + (uint32_t)i * 1024u) & mask;
+          if constexpr (KIND == 0) {
+            auto *l = (__attribute__((address_space(3))) void *)(dst + ((i >> 2) & 1) * 4096);
+            const uint32_t vo = (uint32_t)lane * 16u;
+            switch (i & 3) {
+              case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, vo, so, 0, 0); break;
+              case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, vo, so, 1024, 0); break;
+              case 2: __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, vo, so, 2048, 0); break;
+              default: __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, vo, so, 3072, 0); break;
+            }
+          } else if constexpr (KIND == 2) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void *)(dst + (i & 31) * 256), 4,
+                (uint32_t)lane * 4u, so, 0, 0);
+          } else {
+            gv[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)lane * 16u, so, 0);
+          }
+        }
+        if constexpr (KIND == 1) {
+          if (j >= 32 && (j - 32) % LSP == 0 && (j - 32) / LSP < NLOAD) {
+            const int i = (j - 32) / LSP;
+            *(u32x4 *)(dst + (i & 7) * 1024 + lane * 16) = gv[i];
+          }
+        }
+      }
+      if constexpr (NREAD > 0) {
+        if (j % RSP == RSP / 2 && j / RSP < NREAD) {
+          const int k = j / RSP;
+          rv[k] = *(const u32x4 *)(smem + rd + (k & 7) * 1024);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    base = (base + (uint32_t)NLOAD * 1024u) & mask;
+    if constexpr (NREAD > 0) {
+#pragma unroll
+      for (int k = 0; k < NREAD; ++k) asm volatile("" ::"v"(rv[k]));
+    }
+    if constexpr (KIND != 1 && NLOAD > 0) {
+      // the previous iteration's loads have landed (this one's may run on)
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(NLOAD, 63));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("s_nop 15" ::: "memory");
+  const uint64_t c1 = clock64(), r1 = wall_clock64();
+  float sum = 0.0f;
+  for (int j = 0; j < 16; ++j)
+    for (int e = 0; e < 4; ++e) sum += acc[j][e];
+  out[blockIdx.x * 256 + t] = sum + (float)((const uint32_t *)smem)[t];
+  if (clocks != nullptr && lane == 0) {
+    const int w = blockIdx.x * 4 + wave;
+    clocks[2 * w] = c1 - c0;
+    clocks[2 * w + 1] = r1 - r0;
+  }
+}
+
+using MixFn = void (*)(const uint16_t *, uint32_t, int, float *, uint64_t *);
+template <int KIND, int NREAD, bool BAR = false>
+MixFn mix_fn(int nload) {
+  switch (nload) {
+    case 0: return &probe_mix_kernel<KIND, 0, NREAD, BAR>;
+    case 2: return &probe_mix_kernel<KIND, 2, NREAD, BAR>;
+    case 4: return &probe_mix_kernel<KIND, 4, NREAD, BAR>;
+    case 8: return &probe_mix_kernel<KIND, 8, NREAD, BAR>;
+    case 16: return &probe_mix_kernel<KIND, 16, NREAD, BAR>;
+    default: return nullptr;
+  }
+}
+
 template <int PATTERN>
 __global__ __launch_bounds__(256) void probe_lds_read_kernel(int iters, float *out) {
   __shared__ __attribute__((aligned(16))) char smem[65536];
@@ -527,6 +664,33 @@ hgemm_status_t hgemm_probe_l2_read(int workgroups, int iters, int mode, const vo
     case 3: hipLaunchKernelGGL((probe_l2_kernel<1, 8>), dim3(workgroups), dim3(256), 0, s, b, window_bytes, row_stride, iters, out); break;
     default: return HGEMM_ERR_INVALID_ARG;
   }
+  return launched();
+}
+
+
+hgemm_status_t hgemm_probe_mix(int kind, int nload, int nread, int workgroups, int iters,
+                               const void *buf, uint32_t window_bytes, float *out,
+                               uint64_t *clocks, void *stream) {
+  clear_error();
+  if (workgroups <= 0 || iters <= 0 || !buf || !out || !clocks) return HGEMM_ERR_INVALID_ARG;
+  if (window_bytes < 65536u || window_bytes > (1u << 30) || (window_bytes & (window_bytes - 1)))
+    return HGEMM_ERR_INVALID_ARG;
+  if (((uintptr_t)buf) & 15) return HGEMM_ERR_UNSUPPORTED;
+  MixFn fn = nullptr;
+  if (nread == 0) {
+    fn = kind == 0 ? mix_fn<0, 0>(nload) : kind == 1 ? mix_fn<1, 0>(nload)
+         : kind == 2 ? mix_fn<2, 0>(nload) : nullptr;
+  } else if (nread == 16) {
+    fn = kind == 0 ? mix_fn<0, 16>(nload) : kind == 1 ? mix_fn<1, 16>(nload)
+         : kind == 2 ? mix_fn<2, 16>(nload) : nullptr;
+  } else if (nread == 16 + 256) {  // with a workgroup barrier every 128 MFMAs
+    fn = kind == 0 ? mix_fn<0, 16, true>(nload) : nullptr;
+  } else if (nread == 256) {
+    fn = kind == 0 ? mix_fn<0, 0, true>(nload) : nullptr;
+  }
+  if (fn == nullptr) return HGEMM_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(fn, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
+                     (const uint16_t *)buf, window_bytes, iters, out, clocks);
   return launched();
 }
 

@@ -107,6 +107,8 @@ def _lib() -> ctypes.CDLL:
     lib.hgemm_probe_lds_read.restype = i32
     lib.hgemm_probe_l2_read.argtypes = [i32, i32, i32, vp, ctypes.c_uint32, ctypes.c_uint32, vp, vp]
     lib.hgemm_probe_l2_read.restype = i32
+    lib.hgemm_probe_mix.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.c_uint32, vp, vp, vp]
+    lib.hgemm_probe_mix.restype = i32
     lib.hgemm_probe_pp_offsets.argtypes = [ip, ip, ip]
     lib.hgemm_probe_pp_offsets.restype = i32
     lib.hgemm_probe_lds_offsets.argtypes = [i32, i32, ip]

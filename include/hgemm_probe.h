@@ -167,6 +167,27 @@ hgemm_status_t hgemm_probe_l2_read(int workgroups, int iters, int mode, const vo
                                    void *stream);
 
 /*
+ * Matrix-core issue rate with memory instructions mixed in (one wave per
+ * SIMD, four waves per workgroup): every iteration issues 64 16x16x32 FP16
+ * MFMAs with random operands and, spread evenly among them, `nload` loads
+ * (0, 2, 4, 8 or 16) out of the L2-resident window [buf, buf + window_bytes)
+ * (a power of two, 64 KiB .. 1 GiB) and `nread` (0 or 16) 16-byte LDS reads:
+ *   kind 0: 16-byte-per-lane loads straight into LDS (1 KiB each),
+ *   kind 1: 16-byte-per-lane loads into registers, then written to LDS,
+ *   kind 2: 4-byte-per-lane loads straight into LDS (256 bytes each).
+ * nread + 256 (kind 0 only) adds a workgroup barrier every 128 MFMAs, in the
+ * middle of every other iteration, after waiting for the previous iteration's
+ * loads and this wave's LDS reads (the waits of a pipelined GEMM step).
+ * clocks[2w], clocks[2w+1] (device, 2 * 4 * workgroups uint64_t): shader clock
+ * cycles and 100 MHz real-time ticks of wave w over its loop; cycles divided
+ * by 64 * iters is the time per MFMA, 16 at full rate.  out: workgroups*256
+ * floats (results kept live).
+ */
+hgemm_status_t hgemm_probe_mix(int kind, int nload, int nread, int workgroups, int iters,
+                               const void *buf, uint32_t window_bytes, float *out,
+                               uint64_t *clocks, void *stream);
+
+/*
  * Host-only: byte offset, inside one LDS stage, of 16-byte chunk c of tile
  * row r under LDS layout `lds_layout` (as in hgemm_probe_lds_roundtrip), for
  * r < rows and c < 8: offsets[r * 8 + c].  No GPU work.
