@@ -620,6 +620,22 @@ def clock_trace(widx: int, launches: int, idle_s: float = 2.0) -> int:
                           "dur_us_median": round(float(np.median(dur)), 2),
                           "sclk_mhz": round(float(np.median(mhz))),
                           "tflops": round(w.flops / float(np.median(dur)) / 1e6, 1)}), flush=True)
+    # the second half of the launches, per XCD (workgroup b is dispatched to XCD b mod 8):
+    # engine clock, median shader cycles per workgroup, and the sum of workgroup times over
+    # 256 CUs x the launch time (how much of the launch the CUs spend inside a tile)
+    late = t[launches // 2:]
+    xcd = np.arange(tiles) % 8
+    cyc = late[..., 2] - late[..., 0]
+    real = late[..., 3] - late[..., 1]
+    span = late[..., 3].max(axis=1) - late[..., 1].min(axis=1)
+    print(json.dumps({"clock_trace_xcd": w.name, "launches": [launches // 2, launches - 1],
+                      "sclk_mhz_per_xcd": [round(float(cyc[:, xcd == x].sum() / real[:, xcd == x].sum()
+                                                        * 100.0)) for x in range(8)],
+                      "kcycles_per_workgroup_per_xcd": [round(float(np.median(cyc[:, xcd == x])) / 1e3, 1)
+                                                        for x in range(8)],
+                      "workgroup_time_over_cu_time": round(float(np.median(real.sum(axis=1) /
+                                                                           (256.0 * span))), 4)}),
+          flush=True)
     return 0
 
 
