@@ -158,14 +158,20 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T:
         if constexpr (GEN) asm volatile("" ::: "memory");
       }
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-      // each row of the wave block is WTN*2 bytes = WTN/8 lanes of 16 bytes
+      // each row of the wave block is WTN*2 bytes = WTN/8 lanes of 16 bytes.
+      // C is written once and not read again by this launch: nontemporal
+      // stores stream it past the L2, where it would otherwise evict the A and
+      // B panel lines that neighbouring tiles still read, and leave dirty
+      // lines for the end of the launch to write back (measured: TN f16 8192^3
+      // 740 -> 725 us, NN bf16 4096^3 98.4 -> 97.4, TN f16 2048^3 18.3 -> 18.0;
+      // the same bits)
       constexpr int LPR = T::WTN / 8, RPI = 64 / LPR;
 #pragma unroll
       for (int r = 0; r < T::WTM / RPI; ++r) {
         const int row = r * RPI + lane / LPR, col = 8 * (lane % LPR);
         const u32x4 v = *(const u32x4 *)(cw + row * T::CROW + col * 2);
         const int m = wm0 + row, n = wn0 + col;
-        if (m < M && n < N) *(u32x4 *)(args.C + (size_t)m * ldc + n) = v;
+        if (m < M && n < N) __builtin_nontemporal_store(v, (u32x4 *)(args.C + (size_t)m * ldc + n));
       }
     } else {
 #pragma unroll
@@ -690,7 +696,7 @@ __global__ __launch_bounds__(256) void gemm_sk_fixup(GemmArgs args) {
     u32x2 v;
     v[0] = pack2<DT>(x[0], x[1]);
     v[1] = pack2<DT>(x[2], x[3]);
-    *(u32x2 *)cp = v;
+    __builtin_nontemporal_store(v, (u32x2 *)cp);  // written once, as in store_tile
   }
 }
 
