@@ -137,8 +137,9 @@ def check_kernel(lines) -> list:
 
 def loop_vmcnt_zero(lines) -> int:
     """Number of waits for every outstanding vector-memory operation inside
-    the kernel's loops: the lines from a loop header label to the last
-    branch (conditional or not) back to it."""
+    the kernel's main loops: the lines from a loop header label to the last
+    branch (conditional or not) back to it, for loops that issue matrix-core
+    instructions (a retry loop around an atomic has to wait for its result)."""
     count = 0
     for h, raw in enumerate(lines):
         m = _LABEL.match(raw)
@@ -149,8 +150,19 @@ def loop_vmcnt_zero(lines) -> int:
                 and l.split(";")[0].strip().endswith(header)]
         if not back:
             continue
-        for l in lines[h + 1:back[-1] + 1]:
-            s = l.split(";")[0].strip()
+        body = [l.split(";")[0].strip() for l in lines[h + 1:back[-1] + 1]]
+        if not any(b.startswith("v_mfma") for b in body):
+            continue
+        for s in body:
             if s.startswith("s_waitcnt") and "vmcnt(0)" in s:
                 count += 1
     return count
+
+
+_ACC_STORE = re.compile(r"global_store_dwordx4 v\[\d+:\d+\], (a\[\d+:\d+\]), off\b")
+
+
+def acc_store_sources(lines) -> list:
+    """The accumulator registers each partial-sum store (inline assembly,
+    storing straight from AGPRs) reads, in order."""
+    return [m.group(1) for l in lines for m in [_ACC_STORE.search(l.split(";")[0])] if m]

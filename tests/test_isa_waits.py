@@ -104,3 +104,21 @@ def test_checker_follows_the_back_edge():
     assert not isa_waits.check_kernel(_k(fixed))
     assert isa_waits.loop_vmcnt_zero(_k(body)) == 0
     assert isa_waits.loop_vmcnt_zero(_k(body[:3] + ["s_waitcnt vmcnt(0)"] + body[3:])) == 1
+
+
+def test_partial_sum_stores_read_accumulators_in_place(kernels):
+    """The K-segment kernels store their FP32 partial sums with inline assembly
+    straight from the accumulator registers.  The compiler does not see those
+    stores, so it pads no wait states around them: if it moved accumulators
+    through a scratch register range for them (it does when the accumulators
+    stay live afterwards), a later write could overwrite store data not yet
+    read.  Every such store must read registers of its own."""
+    checked = 0
+    for name, lines in kernels.items():
+        src = isa_waits.acc_store_sources(lines)
+        if not src:
+            continue
+        checked += 1
+        dup = {r for r in src if src.count(r) > 1}
+        assert not dup, f"{name}: accumulator registers stored more than once: {sorted(dup)[:4]}"
+    assert checked >= 20
