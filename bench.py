@@ -176,21 +176,29 @@ def micro() -> int:
     names = {0: "lane-contiguous", 1: "baseline 32-row fragments, XOR", 2: "baseline, plain",
              3: "baseline, XOR by row", 4: "production 16-row fragments, XOR",
              5: "production 16-row fragments, plain", 6: "production transposing read, XOR",
-             7: "production transposing read, plain"}
+             7: "production transposing read, plain", 8: "16-row fragments on 64-byte rows"}
     wg, it = 512, 2000
     lout = torch.empty(wg * 256, device="cuda")
-    for pat in range(8):
+    for pat in range(9):
         ms = timed(lambda: lib.hgemm_probe_lds_read(wg, it, pat, lout.data_ptr(), sp))
         byts = wg * 256 * it * 16 * 16
         emit({"micro": "lds_read", "pattern": pat, "what": names[pat], "ms": round(ms, 4),
               "tb_per_s": round(byts / ms / 1e9, 2)})
+    # which 16 lanes the LDS serves together for 16-byte reads: one pattern per
+    # candidate grouping, free of bank conflicts only under that grouping
+    for basis in LDS_LANE_GROUPINGS:
+        offs = torch.tensor(lds_lane_pattern(basis), dtype=torch.int32, device="cuda")
+        ms = timed(lambda: lib.hgemm_probe_lds_lanes(wg, it, offs.data_ptr(), lout.data_ptr(), sp))
+        emit({"micro": "lds_lanes", "grouping": list(basis), "ms": round(ms, 4),
+              "tb_per_s": round(wg * 256 * it * 16 * 16 / ms / 1e9, 2)})
     # L2-to-CU streaming out of an L2-resident 4 MiB window (each workgroup's
     # 64 KiB slides by 1 KiB per iteration), rows contiguous or 16 KiB apart
     # (one K step of a K = 8192 operand panel)
     window = 4 << 20
     buf = torch.empty(window, dtype=torch.uint8, device="cuda")
     for stride in (128, 16384):
-        for mode, what in ((0, "registers"), (1, "direct-to-LDS")):
+        for mode, what in ((0, "registers"), (1, "direct-to-LDS"),
+                           (4, "registers, 64-byte halves"), (5, "direct-to-LDS, 64-byte halves")):
             wgs, its = 1024, 256
             ms = timed(lambda: lib.hgemm_probe_l2_read(wgs, its, mode, buf.data_ptr(), window,
                                                        stride, lout.data_ptr(), sp))
@@ -492,13 +500,71 @@ def settle(launch, settle_ms: float):
     return n, round((time.perf_counter() - t0) * 1e3, 1)
 
 
+# Candidate 16-lane groupings of the LDS's 16-byte reads: the cosets of the
+# span of these lane-index XOR masks (the groupings under which the measured
+# rates of the fixed read patterns all come out right).
+LDS_LANE_GROUPINGS = [(1, 2, 8, 20), (2, 5, 9, 17), (2, 8, 20, 37), (2, 12, 20, 37),
+                      (1, 2, 12, 20), (2, 8, 20, 33), (2, 5, 8, 17), (2, 12, 20, 33)]
+
+
+def lds_lane_pattern(basis, seed: int = 0):
+    """64 per-lane byte offsets free of bank conflicts if the LDS serves the
+    cosets of span(basis) together: coset g (in order of its smallest lane)
+    covers the 16 16-byte bank groups of bytes [256g, 256g + 256) once, in a
+    seeded random order (which makes the pattern conflict at least two-way
+    under each other candidate)."""
+    import numpy as np
+    span = {0}
+    for v in basis:
+        span |= {x ^ v for x in span}
+    rng = np.random.default_rng(seed)
+    offs, seen, g = [0] * 64, set(), 0
+    for l0 in range(64):
+        if l0 in seen:
+            continue
+        grp = sorted(l0 ^ v for v in span)
+        seen |= set(grp)
+        order = rng.permutation(16)
+        for i, lane in enumerate(grp):
+            offs[lane] = 256 * g + 16 * int(order[i])
+        g += 1
+    return offs
+
+
+class QueueHold:
+    """One long launch of the matrix-core rate probe (random FP16 operands,
+    one wave per SIMD, so the board draws about what a GEMM draws) that keeps
+    the GPU busy while the host enqueues a run of short launches behind it.
+    Without it, a kernel shorter than the host's launch path (the ctypes call
+    and two event records) leaves the GPU idle between an event and its
+    kernel, and the event pair measures that gap too."""
+
+    US_PER_ITER = 0.15  # 1024 waves x 16 MFMAs of 16x16x32 per iteration, about 1.8 PFLOP/s
+
+    def __init__(self):
+        import torch
+        self.out = torch.empty(1024 * 64, device="cuda")
+        self.clocks = torch.empty(2 * 1024, dtype=torch.int64, device="cuda")
+
+    def hold(self, ms: float):
+        import torch
+        from dense_half_precision_amd import hgemm
+        iters = max(8, int(ms * 1e3 / self.US_PER_ITER) // 8 * 8)
+        st = hgemm.lib().hgemm_probe_mfma_rate(1, 1, 1024, iters, self.out.data_ptr(),
+                                               self.clocks.data_ptr(),
+                                               torch.cuda.current_stream().cuda_stream)
+        if st != hgemm.OK:
+            raise hgemm.HgemmError(st, "queue hold")
+
+
 def time_workload(w, dA, dB, dC, steps: int, warmup: int, settle_ms: float = 0.0):
     """The automatic choice on one workload: settle, the engine clock
     (measurement copy, enqueued with no gap), `warmup` launches, then `steps`
     launches with HIP events on the launch stream around each, then `steps`
-    launches back to back without events (wall clock between
-    synchronisations).  Returns (kernel name, per-launch ms, back-to-back ms
-    per launch, MHz)."""
+    launches back to back between one pair of events.  Both runs are queued
+    behind a QueueHold launch, so that the GPU executes them back to back
+    whatever the host's launch rate.  Returns (kernel name, per-launch ms,
+    back-to-back ms per launch, MHz)."""
     import numpy as np
     import torch
     from dense_half_precision_amd import hgemm
@@ -518,6 +584,8 @@ def time_workload(w, dA, dB, dC, steps: int, warmup: int, settle_ms: float = 0.0
     for _ in range(warmup):
         fn(*args)
     torch.cuda.synchronize()
+    hold = QueueHold()
+    hold.hold(steps * 0.05)  # 50 us of host time per launch and its two events
     for a, b in ev:
         a.record(stream)
         st = fn(*args)
@@ -525,11 +593,14 @@ def time_workload(w, dA, dB, dC, steps: int, warmup: int, settle_ms: float = 0.0
         if st != hgemm.OK:
             raise hgemm.HgemmError(st, "workload launch")
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold.hold(steps * 0.03)
+    e0.record(stream)
     for _ in range(steps):
         fn(*args)
+    e1.record(stream)
     torch.cuda.synchronize()
-    b2b = (time.perf_counter() - t0) * 1e3 / steps
+    b2b = e0.elapsed_time(e1) / steps
     return kname, np.array([a.elapsed_time(b) for a, b in ev]), b2b, clk.mhz()
 
 

@@ -82,6 +82,12 @@ constexpr KernelEntry pp_entry(const char *name, int group_m) {
   return KernelEntry{name, kTN, DT, PpCfg::BM, PpCfg::BN, PpCfg::BK, PpCfg::LDS, group_m, false,
                      true, &gemm_pp_kernel<DT>, nullptr, nullptr, nullptr, PpCfg::NT};
 }
+template <int DT>
+constexpr KernelEntry pp_timed_entry(const char *name, int group_m) {
+  return KernelEntry{name, kTN, DT, PpCfg::BM, PpCfg::BN, PpCfg::BK, PpCfg::LDS, group_m, false,
+                     true, &gemm_pp_kernel<DT, true>, nullptr, nullptr, nullptr, PpCfg::NT,
+                     PpCfg::NSB, false, true};
+}
 // the register-staged baseline assumes packed TN/NN operands, alpha 1, beta 0
 template <class T, int LAYOUT, int DT>
 constexpr KernelEntry rs_entry(const char *name, int group_m) {
@@ -172,6 +178,8 @@ const KernelEntry kTable[] = {
     timed_entry<T256, kNN, kBF16>("nn_bf16_256x256x64_clk", 4),
     timed_entry<T128R3, kTN, kF16>("tn_f16_128x128x64_r3_clk", 4),
     timed_entry<T64, kTN, kF16>("tn_f16_64x64x64_clk", 4),
+    pp_timed_entry<kF16>("tn_f16_256x256x64_pp_clk", 4),
+    pp_timed_entry<kBF16>("tn_bf16_256x256x64_pp_clk", 4),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 

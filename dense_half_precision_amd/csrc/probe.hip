@@ -9,7 +9,6 @@
 
 #include "hgemm_probe.h"
 #include "gemm_regstage.hpp"
-#include "gemm_pp_kernel.hpp"
 
 namespace {
 
@@ -422,9 +421,54 @@ __global__ __launch_bounds__(256) void probe_lds_read_kernel(int iters, float *o
   out[blockIdx.x * 256 + t] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
 }
 
+// The 16-row fragment read on 64-byte rows (32 k per row, chunk c of row r
+// at c ^ ((r >> 2) & 3)): lane l reads row l % 16, logical chunk l / 16.
+// That layout is conflict-free if 16-byte reads were served lanes 0-15,
+// 16-31, ... at a time, and measures at half the rate of the production
+// layout: the hardware groups the lanes otherwise.  16 fragments of 16 rows
+// per iteration, each wave in its own 16 KiB quarter.
+__global__ __launch_bounds__(256) void probe_lds_half_row_kernel(int iters, float *out) {
+  __shared__ __attribute__((aligned(1024))) char smem[65536];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int i = t; i < 65536 / 16; i += 256) ((u32x4 *)smem)[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  const int row = lane & 15, chunk = (lane >> 4) ^ ((row >> 2) & 3);
+  const char *q = smem + wave * 16384 + row * 64 + chunk * 16;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc ^= *(const u32x4 *)(q + j * 1024);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  }
+  out[blockIdx.x * 256 + t] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+}
+
+// 16-byte LDS reads at per-lane byte offsets given by the caller (lane l reads
+// offs[l] + 1024 * j, j = 0..15, within its wave's 16 KiB quarter; every
+// read of an iteration at its own address, so that none can be folded into
+// another): the read rate of any lane-to-address map, for the bank model.
+__global__ __launch_bounds__(256) void probe_lds_lanes_kernel(int iters, const uint32_t *offs,
+                                                              float *out) {
+  __shared__ __attribute__((aligned(1024))) char smem[65536];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int i = t; i < 65536 / 16; i += 256) ((u32x4 *)smem)[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  const char *q = smem + wave * 16384 + (offs[lane] & 1008u);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc ^= *(const u32x4 *)(q + j * 1024);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  }
+  out[blockIdx.x * 256 + t] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+}
+
 // Streams 64 KiB per workgroup per iteration out of an L2-resident window:
 // MODE 0 into registers, MODE 1 straight into LDS; NF loads per lane in flight.
-template <int MODE, int NF>
+// HALF: every load covers 16 half rows of 64 bytes instead of 8 rows of 128,
+// and two consecutive iterations take the two halves of the same rows, so
+// that each 128-byte line is requested twice.
+template <int MODE, int NF, bool HALF = false>
 __global__ __launch_bounds__(256) void probe_l2_kernel(const uint16_t *buf, uint32_t window,
                                                        uint32_t row_stride, int iters, float *out) {
   __shared__ __attribute__((aligned(1024))) char smem[65536];
@@ -440,9 +484,14 @@ __global__ __launch_bounds__(256) void probe_l2_kernel(const uint16_t *buf, uint
       u32x4 v[NF];
 #pragma unroll
       for (int i = 0; i < NF; ++i) {
-        // 1 KiB per wave and load: 8 rows of 128 bytes, rows row_stride bytes apart
-        const uint32_t off = (base + (uint32_t)(wave * 16 + j + i) * 8u * row_stride +
-                              (uint32_t)(lane >> 3) * row_stride + (uint32_t)(lane & 7) * 16u) & mask;
+        // 1 KiB per wave and load: 8 rows of 128 bytes (or 16 of 64), rows
+        // row_stride bytes apart
+        const uint32_t off =
+            HALF ? (base + (uint32_t)(it & 1) * 64u +
+                    ((uint32_t)(wave * 16 + j + i) * 16u + (uint32_t)(lane >> 2)) * row_stride +
+                    (uint32_t)(lane & 3) * 16u) & mask
+                 : (base + (uint32_t)(wave * 16 + j + i) * 8u * row_stride +
+                    (uint32_t)(lane >> 3) * row_stride + (uint32_t)(lane & 7) * 16u) & mask;
         if constexpr (MODE == 0) v[i] = load16(r, off);
         else load16_lds(r, off, smem + (wave * 16 + j + i) * 1024);
       }
@@ -452,7 +501,7 @@ __global__ __launch_bounds__(256) void probe_l2_kernel(const uint16_t *buf, uint
       }
     }
     if constexpr (MODE == 1) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    base = (base + 128u * 8u) & mask;  // next 128-byte column of the same rows
+    if (!HALF || (it & 1)) base = (base + 128u * 8u) & mask;  // 1 KiB further along the rows
   }
   if constexpr (MODE == 1) {
     __syncthreads();
@@ -565,15 +614,6 @@ hgemm_status_t hgemm_probe_operand_offsets(int mn_major, int bx, int *load_row, 
   return HGEMM_OK;
 }
 
-hgemm_status_t hgemm_probe_pp_offsets(int *load_row, int *load_chunk, int *read_off) {
-  if (!load_row || !load_chunk || !read_off) return HGEMM_ERR_INVALID_ARG;
-  for (int seg = 0; seg < 16; ++seg)
-    for (int l = 0; l < 64; ++l) pp_load_place(seg, l, load_row[seg * 64 + l], load_chunk[seg * 64 + l]);
-  for (int f = 0; f < 16; ++f)
-    for (int l = 0; l < 64; ++l) read_off[f * 64 + l] = f * 1024 + (int)pp_frag_offset(l);
-  return HGEMM_OK;
-}
-
 hgemm_status_t hgemm_probe_lds_roundtrip(int lds_layout, const void *src, void *dst,
                                          void *stream) {
   clear_error();
@@ -641,8 +681,18 @@ hgemm_status_t hgemm_probe_lds_read(int workgroups, int iters, int pattern, floa
     case 5: hipLaunchKernelGGL((probe_lds_frag_kernel<false, false>), dim3(workgroups), dim3(256), 0, s, iters, out); break;
     case 6: hipLaunchKernelGGL((probe_lds_frag_kernel<true, true>), dim3(workgroups), dim3(256), 0, s, iters, out); break;
     case 7: hipLaunchKernelGGL((probe_lds_frag_kernel<true, false>), dim3(workgroups), dim3(256), 0, s, iters, out); break;
+    case 8: hipLaunchKernelGGL(probe_lds_half_row_kernel, dim3(workgroups), dim3(256), 0, s, iters, out); break;
     default: return HGEMM_ERR_INVALID_ARG;
   }
+  return launched();
+}
+
+hgemm_status_t hgemm_probe_lds_lanes(int workgroups, int iters, const uint32_t *lane_offsets,
+                                     float *out, void *stream) {
+  clear_error();
+  if (workgroups <= 0 || iters <= 0 || !lane_offsets || !out) return HGEMM_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(probe_lds_lanes_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
+                     iters, lane_offsets, out);
   return launched();
 }
 
@@ -662,6 +712,8 @@ hgemm_status_t hgemm_probe_l2_read(int workgroups, int iters, int mode, const vo
     case 1: hipLaunchKernelGGL((probe_l2_kernel<1, 16>), dim3(workgroups), dim3(256), 0, s, b, window_bytes, row_stride, iters, out); break;
     case 2: hipLaunchKernelGGL((probe_l2_kernel<0, 8>), dim3(workgroups), dim3(256), 0, s, b, window_bytes, row_stride, iters, out); break;
     case 3: hipLaunchKernelGGL((probe_l2_kernel<1, 8>), dim3(workgroups), dim3(256), 0, s, b, window_bytes, row_stride, iters, out); break;
+    case 4: hipLaunchKernelGGL((probe_l2_kernel<0, 16, true>), dim3(workgroups), dim3(256), 0, s, b, window_bytes, row_stride, iters, out); break;
+    case 5: hipLaunchKernelGGL((probe_l2_kernel<1, 16, true>), dim3(workgroups), dim3(256), 0, s, b, window_bytes, row_stride, iters, out); break;
     default: return HGEMM_ERR_INVALID_ARG;
   }
   return launched();

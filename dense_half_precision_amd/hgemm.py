@@ -105,12 +105,12 @@ def _lib() -> ctypes.CDLL:
     lib.hgemm_probe_mfma_rate.restype = i32
     lib.hgemm_probe_lds_read.argtypes = [i32, i32, i32, vp, vp]
     lib.hgemm_probe_lds_read.restype = i32
+    lib.hgemm_probe_lds_lanes.argtypes = [i32, i32, vp, vp, vp]
+    lib.hgemm_probe_lds_lanes.restype = i32
     lib.hgemm_probe_l2_read.argtypes = [i32, i32, i32, vp, ctypes.c_uint32, ctypes.c_uint32, vp, vp]
     lib.hgemm_probe_l2_read.restype = i32
     lib.hgemm_probe_mix.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.c_uint32, vp, vp, vp]
     lib.hgemm_probe_mix.restype = i32
-    lib.hgemm_probe_pp_offsets.argtypes = [ip, ip, ip]
-    lib.hgemm_probe_pp_offsets.restype = i32
     lib.hgemm_probe_lds_offsets.argtypes = [i32, i32, ip]
     lib.hgemm_probe_lds_offsets.restype = i32
     lib.hgemm_probe_tile_order.argtypes = [i32, i32, i32, i32, ip, ip]
@@ -364,16 +364,6 @@ def operand_offsets(mn_major: int, bx: int):
            "hgemm_probe_operand_offsets")
     return (np.array(lr).reshape(bx // 8, 64), np.array(lc).reshape(bx // 8, 64),
             np.array(ro).reshape(bx // 16, 2, reads, 64))
-
-
-def pp_offsets():
-    """The two-group kernel's LDS placement of one 32-k slice (host-side code):
-    (load_row, load_chunk) per [segment][lane], read_off per [fragment][lane]."""
-    import numpy as np
-    lr, lc, ro = ((ctypes.c_int * 1024)() for _ in range(3))
-    _check(_lib().hgemm_probe_pp_offsets(lr, lc, ro), "hgemm_probe_pp_offsets")
-    return (np.array(lr).reshape(16, 64), np.array(lc).reshape(16, 64),
-            np.array(ro).reshape(16, 64))
 
 
 def lds_offsets(lds_layout, rows=256):

@@ -201,7 +201,8 @@ hgemm_status_t hgemm_gemm_ws(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t 
 /* As hgemm_gemm_ws, with an explicit configuration (NULL = automatic);
  * cfg->split > 0 forces that split (HGEMM_ERR_UNSUPPORTED when there is no
  * tail, S exceeds the K steps, or the workspace is too small).  A "_clk"
- * kernel (a measurement copy of a production kernel) writes four uint64_t
+ * kernel (a measurement copy of a production kernel or of the two-group
+ * "_pp" kernel) writes four uint64_t
  * per workgroup b to the workspace at index 4b: shader clock and 100 MHz
  * real-time clock before the tile, then both after its stores of C are
  * issued; it needs 32 bytes per workgroup (HGEMM_ERR_UNSUPPORTED otherwise). */
@@ -249,7 +250,8 @@ int hgemm_kernel_count(void);
  * entries 38..45, see hgemm_auto_kernel; "at_" layouts take A stored
  * transposed), with a suffix naming what an
  * ablation changes ("_plainlds": LDS without the XOR swizzle, "_directepi":
- * epilogue without LDS staging), and an "rs_" prefix for the register-staged
+ * epilogue without LDS staging, "_pp": eight waves in two groups alternating
+ * memory and MFMA phases), and an "rs_" prefix for the register-staged
  * 32x32x16 baseline design (suffix: its LDS layout), and a "_clk" suffix for
  * measurement copies that record per-workgroup clocks (see hgemm_gemm_ws_ex).
  * The integers describing

@@ -78,20 +78,6 @@ hgemm_status_t hgemm_probe_operand_offsets(int mn_major, int bx, int *load_row, 
                                            int *read_off);
 
 /*
- * Host-side: the LDS placement of one 32-k slice of an operand in the
- * two-group ("ping-pong") kernel, computed by the functions that kernel uses
- * (a slot of 256 rows of 64 bytes).
- *   load_row[s*64 + l], load_chunk[s*64 + l] (16 segments x 64 lanes): the
- *     row and the logical 16-byte chunk (k = 8*chunk .. +7 of the slice) that
- *     lane l of direct-to-LDS segment s loads; it lands at LDS byte
- *     s*1024 + 16*l of the slot.
- *   read_off[f*64 + l] (16 fragments x 64 lanes): the LDS byte offset lane l
- *     reads (16 bytes) for the fragment of rows 16f .. 16f+15.
- * All three are host arrays of 1024 ints.  No GPU work.
- */
-hgemm_status_t hgemm_probe_pp_offsets(int *load_row, int *load_chunk, int *read_off);
-
-/*
  * LDS layout round trip for a 256-row x 64-column tile of 16-bit values:
  * the tile is written to LDS with the register-staged baseline's store pattern and LDS layout
  * `lds_layout` (0 = XOR swizzle on row/2, 1 = plain rows, 2 = padded rows,
@@ -142,12 +128,25 @@ hgemm_status_t hgemm_probe_mfma_rate(int shape, int random, int waves, int iters
  *              with the XOR layout,  pattern 5: the same on plain rows,
  *   pattern 6: the production transposing fragment read (two 8-byte
  *              ds_read_b64_tr_b16 per 16 bytes) on 256-byte k-rows with the
- *              XOR layout,  pattern 7: the same without it.
+ *              XOR layout,  pattern 7: the same without it;
+ *   pattern 8: the 16-row fragment read on 64-byte rows (32 k per row, chunk
+ *              c of row r at c ^ ((r >> 2) & 3)).
  * Bytes read = workgroups * 256 * iters * 16 * 16 for every pattern.
  * out: workgroups*256 floats.
  */
 hgemm_status_t hgemm_probe_lds_read(int workgroups, int iters, int pattern, float *out,
                                     void *stream);
+
+/*
+ * LDS read throughput of an arbitrary lane-to-address map: 256 threads per
+ * workgroup, each wave in its own 16 KiB quarter of a 64 KiB buffer; lane l
+ * reads 16 bytes at (lane_offsets[l] & 1008) + 1024 * j, j = 0..15, `iters`
+ * times.  lane_offsets: 64 uint32_t in device memory (offsets into the first
+ * KiB; the mask keeps every read inside the quarter).  Bytes read = workgroups * 256 * iters *
+ * 16 * 16.  out: workgroups*256 floats.
+ */
+hgemm_status_t hgemm_probe_lds_lanes(int workgroups, int iters, const uint32_t *lane_offsets,
+                                     float *out, void *stream);
 
 /*
  * Global-to-CU streaming throughput: every workgroup of 256 threads moves
@@ -159,7 +158,10 @@ hgemm_status_t hgemm_probe_lds_read(int workgroups, int iters, int pattern, floa
  * operand); successive iterations move to the next 128-byte column.
  *   mode 0: into registers, 16 loads per lane in flight,
  *   mode 1: straight into LDS (direct-to-LDS loads), 16 in flight,
- *   mode 2: into registers, 8 in flight,  mode 3: into LDS, 8 in flight.
+ *   mode 2: into registers, 8 in flight,  mode 3: into LDS, 8 in flight;
+ *   mode 4 / 5: as mode 0 / 1, but each load reads 16 half rows of 64 bytes
+ *   and two consecutive iterations read the two halves of the same rows, so
+ *   that every 128-byte line is requested twice.
  * Bytes moved = workgroups * iters * 65536.  out: workgroups*256 floats.
  */
 hgemm_status_t hgemm_probe_l2_read(int workgroups, int iters, int mode, const void *buf,

@@ -15,6 +15,8 @@ pytestmark = pytest.mark.gpu
     ("nn_bf16_256x256x64", "nn", "bf16", (300, 512, 136)),
     ("tn_f16_128x128x64_r3", "tn", "f16", (264, 392, 1608)),
     ("tn_f16_64x64x64", "tn", "f16", (136, 200, 72)),
+    ("tn_f16_256x256x64_pp", "tn", "f16", (520, 776, 200)),
+    ("tn_bf16_256x256x64_pp", "tn", "bf16", (300, 512, 1000)),
 ])
 def test_clock_copy_matches_production(name, layout, dtype, shape):
     import torch

@@ -134,11 +134,33 @@ def test_mfma_rate_probe_runs(shape, random):
     assert (c[:, 0] > 0).all() and (c[:, 1] > 0).all()
 
 
-@pytest.mark.parametrize("pattern", range(8))
+@pytest.mark.parametrize("pattern", range(9))
 def test_lds_read_probe_runs(pattern):
     import torch
     out = torch.full((2 * 256,), float("nan"), device="cuda")
     assert hgemm.lib().hgemm_probe_lds_read(2, 3, pattern, out.data_ptr(),
                                             helpers.stream_ptr()) == hgemm.OK
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("mode", range(6))
+def test_l2_read_probe_runs(mode):
+    import torch
+    window = 1 << 20
+    buf = torch.zeros(window, dtype=torch.uint8, device="cuda")
+    out = torch.full((2 * 256,), float("nan"), device="cuda")
+    assert hgemm.lib().hgemm_probe_l2_read(2, 3, mode, buf.data_ptr(), window, 16384,
+                                           out.data_ptr(), helpers.stream_ptr()) == hgemm.OK
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+
+
+def test_lds_lanes_probe_runs():
+    import torch
+    offs = torch.tensor([16 * ((7 * l) % 64) for l in range(64)], dtype=torch.int32, device="cuda")
+    out = torch.full((2 * 256,), float("nan"), device="cuda")
+    assert hgemm.lib().hgemm_probe_lds_lanes(2, 3, offs.data_ptr(), out.data_ptr(),
+                                             helpers.stream_ptr()) == hgemm.OK
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
