@@ -646,6 +646,79 @@ def all_workloads(headline_index: int, headline_line: dict, settle_ms: float):
     return lines
 
 
+def phases(widx: int, launches: int, settle_ms: float) -> int:
+    """Where the main loop's cycles go: after the settle phase, `launches`
+    launches of the workload kernel's "_ph" copy, which reads the shader
+    clock around each K step's wait for the next step's loads (W) and its
+    barrier (B), the rest of the step (R: 128 MFMAs, ideally 2048 cycles, with
+    the fragment reads, loads and address arithmetic among them), then as
+    many of its "_clk" copy (per-workgroup shader cycles of the unchanged
+    kernel).  One JSON line: mean cycles per step of each phase over all
+    waves, their spread over waves, and the unchanged kernel's cycles per
+    step (tile cycles / K steps, prologue and epilogue included)."""
+    import numpy as np
+    import torch
+    from dense_half_precision_amd import hgemm, inputs
+    w = inputs.workload(widx)
+    A, B = inputs.operands(w)
+    dA = torch.from_numpy(A.view(np.int16)).cuda()
+    dB = torch.from_numpy(B.view(np.int16)).cuda()
+    dC = torch.empty((w.M, w.N), dtype=torch.int16, device="cuda")
+    kname = hgemm.kernel_table()[hgemm.auto_kernel(
+        hgemm.TN if w.layout == "tn" else hgemm.NN, w.dtype, w.M, w.N, w.K)]["name"]
+    kph = hgemm.kernel_index(kname + "_ph")
+    info = hgemm.kernel_table()[kph]
+    tiles = -(-w.M // info["bm"]) * -(-w.N // info["bn"])
+    opB = hgemm.OP_T if w.layout == "tn" else hgemm.OP_N
+    ldb = w.K if w.layout == "tn" else w.N
+    sp = torch.cuda.current_stream().cuda_stream
+    args = (hgemm.OP_N, opB, w.M, w.N, w.K, w.dtype, 1.0, dA.data_ptr(), w.K, dB.data_ptr(), ldb,
+            0.0, dC.data_ptr(), w.N)
+    ph = torch.zeros((launches, tiles, 4, 8), dtype=torch.int32, device="cuda")
+    clk = EngineClock(w, dA, dB, dC, kname, launches=launches)
+    fn = hgemm.lib().hgemm_tn if w.layout == "tn" else hgemm.lib().hgemm_nn
+    largs = (w.M, w.N, w.K, hgemm.F16 if w.dtype == "f16" else hgemm.BF16, dA.data_ptr(),
+             dB.data_ptr(), dC.data_ptr(), sp)
+    settle(lambda: fn(*largs), settle_ms)
+    for i in range(launches):
+        st = hgemm.hgemm_gemm_ws(*args, ph[i].data_ptr(), tiles * 128, sp, kernel=kph)
+        if st != hgemm.OK:
+            raise hgemm.HgemmError(st, "phase-clock launch")
+    clk.enqueue()
+    torch.cuda.synchronize()
+    v = ph.cpu().numpy().astype(np.int64).reshape(-1, 8)  # one row per wave
+    kt = v[:, 3]
+    assert (kt == kt[0]).all() and kt[0] > 1
+    KT = int(kt[0])
+    wait, bar, rest = v[:, 0] / KT, v[:, 1] / KT, v[:, 2] / (KT - 1)
+    total = wait + bar + rest
+    # the wait after c also waits for c's own result, and the wait after e
+    # (one MFMA after it) for e's: one clock read's round trip, less one MFMA
+    rt = float(np.median(v[:, 6]))
+    t = clk.ts.cpu().numpy().astype(np.float64)
+    tile_cyc = (t[..., 2] - t[..., 0]).ravel()
+    q = lambda x: [round(float(np.percentile(x, p)), 1) for p in (10, 50, 90)]
+    print(json.dumps({"phases": w.name, "kernel": kname, "launches": launches, "k_steps": KT,
+                      "cycles_per_step": {"wait": round(float(wait.mean()), 1),
+                                          "barrier": round(float(bar.mean()), 1),
+                                          "rest": round(float(rest.mean()), 1),
+                                          "total": round(float(total.mean()), 1),
+                                          "ideal_mfma": 128 * 16},
+                      "p10_p50_p90_over_waves": {"wait": q(wait), "barrier": q(bar),
+                                                 "rest": q(rest), "total": q(total)},
+                      "clock_read_round_trip": rt,
+                      "corrected_cycles_per_step": {
+                          "wait": round(float(wait.mean()) - rt, 1),
+                          "barrier": round(float(bar.mean()), 1),
+                          "rest": round(float(rest.mean()) - max(rt - 16.0, 0.0), 1),
+                          "total": round(float(total.mean()) - rt - max(rt - 16.0, 0.0), 1)},
+                      "last_step_after_barrier": round(float(v[:, 5].mean()), 1),
+                      "loop_cycles_per_step": round(float((v[:, 4] / KT).mean()), 1),
+                      "unchanged_kernel_tile_cycles_per_step": round(float(tile_cyc.mean() / KT), 1),
+                      "sclk_mhz": round(clk.mhz())}), flush=True)
+    return 0
+
+
 def clock_trace(widx: int, launches: int, idle_s: float = 2.0) -> int:
     """The engine clock over a run of back-to-back launches that starts after
     `idle_s` of GPU idle time: the measurement copy of the workload's kernel
@@ -744,6 +817,10 @@ def main() -> int:
     ap.add_argument("--clock-trace", type=int, default=0, metavar="LAUNCHES",
                     help="print the engine clock over this many back-to-back launches of the "
                          "workload's kernel after 2 s idle, and exit")
+    ap.add_argument("--phases", type=int, default=0, metavar="LAUNCHES",
+                    help="after the settle phase, time the main loop's phases (wait, barrier, "
+                         "rest) with the workload kernel's '_ph' copy over this many launches, "
+                         "and exit")
     ap.add_argument("--no-workloads", action="store_true",
                     help="leave out the per-workload list (all five workloads timed after "
                          "the headline run)")
@@ -760,6 +837,11 @@ def main() -> int:
             print("bench.py: one GPU only", file=sys.stderr)
             return 2
         return clock_trace(args.workload, args.clock_trace)
+    if args.phases > 0:
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            return 2
+        return phases(args.workload, args.phases, args.settle_ms)
     if args.mix:
         if args.gpus != 1:
             print("bench.py: one GPU only", file=sys.stderr)

@@ -199,7 +199,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T:
 // SPLIT: only K segment `seg` of sk_split, whose FP32 partial sums go to
 // workspace slot `slot` (a separate instantiation, so that whole-K tiles
 // carry none of the segment bookkeeping in registers).
-template <class T, int LAYOUT, int DT, bool SPLIT, bool OPAQUE = false>
+// PH: a measurement copy that reads the shader clock (s_memtime) at three
+// points of every K step and writes each wave's per-phase cycle sums to
+// ((uint32_t *)args.ws)[8 * (NW * blockIdx.x + wave) ..] (see the main loop).
+template <class T, int LAYOUT, int DT, bool SPLIT, bool OPAQUE = false, bool PH = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int tile, int seg,
                                           int slot) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
@@ -462,6 +465,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   }
   __builtin_amdgcn_sched_barrier(0);
 
+  // ---- phase clocks (PH only) ------------------------------------------------
+  // Stamps per step: c before the wait that ends Y, d after it, e after the
+  // barrier.  s_memtime counts on the LDS/scalar counter, and while one is
+  // outstanding every wait the compiler places for an LDS read becomes a
+  // wait for all of them; so c sits just before the loop's own lgkmcnt(0)
+  // wait, and d and e are retired by one more lgkmcnt(0) after Z's first
+  // MFMA, before Z's first LDS read (the only cost the stamps add: their
+  // round trip, less one MFMA).  Phase sums over the steps:
+  //   W = d - c: the wait for the next step's loads and the own reads,
+  //   B = e - d: the barrier,
+  //   R = next c - e: everything else, i.e. 128 MFMAs with the fragment
+  //       reads, loads and address arithmetic among them (KT - 1 of these).
+  uint32_t ph_w = 0, ph_b = 0, ph_r = 0;
+  uint32_t pc = 0, pd = 0, pe = 0, ph_first = 0;
+  auto stamp = [&]() { return (uint32_t)__builtin_amdgcn_s_memtime(); };
+
   // ---- main loop -------------------------------------------------------------
   // stage offsets of steps kt, kt+1, ..., rotated at the end of each step
   // (no division in the loop); ra[NSA-1] is also the stage of step kt-1
@@ -498,14 +517,31 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
     }
     // step kt+1 complete in LDS (later steps' loads may stay in flight), own
     // reads done
+    if constexpr (PH) pc = stamp();
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(AHEAD, 0));
-    wg_barrier();
+    if constexpr (PH) {
+      if (kt > 0) ph_r += pc - pe;  // e of the step before is in
+      else ph_first = pc;
+      pd = stamp();
+      wg_barrier();
+      pe = stamp();
+    } else {
+      wg_barrier();
+    }
     // Z: second half of slice 1; read slice 0 of step kt+1; B of step kt+NSB
     prep_b(kt + NSB);
     const uint32_t lb = rb[0];  // step kt+NSB reuses the B stage of step kt
 #pragma unroll
     for (int t = NMF / 2; t < NMF; ++t) {
       mfma(I1{}, t);
+      if constexpr (PH) {
+        if (t == NMF / 2) {  // d and e in, before the first read of Z
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+          ph_w += pd - pc;
+          ph_b += pe - pd;
+        }
+      }
       constexpr int H = NMF / 2;
       const int u = t - H;
 #pragma unroll
@@ -522,6 +558,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
 #pragma unroll
     for (int i = 0; i < NSB - 1; ++i) rb[i] = rb[i + 1];
     rb[NSB - 1] = cb;
+  }
+
+  if constexpr (PH) {
+    // the last step's second half of slice 1, up to the end of the loop; then
+    // one stamp's round trip (issue to result), which the wait after c and
+    // the wait after e also contain
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    const uint32_t end = stamp();
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    const uint32_t rt0 = stamp();
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    const uint32_t rt1 = stamp();
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    if (lane == 0) {
+      uint32_t *o = reinterpret_cast<uint32_t *>(args.ws) + 8 * ((size_t)T::NW * blockIdx.x + wave);
+      o[0] = ph_w;
+      o[1] = ph_b;
+      o[2] = ph_r;
+      o[3] = (uint32_t)KT;
+      o[4] = KT > 0 ? end - ph_first : 0u;  // first step's c to the loop's end
+      o[5] = KT > 0 ? end - pe : 0u;        // the last step's Z
+      o[6] = rt1 - rt0;
+      o[7] = 0;
+    }
   }
 
   // The last step (or, for K = 0, the prologue) read fragments for a step that
@@ -580,7 +640,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
 //     real-time clock (s_memrealtime) before its tile and after its stores
 //     of C are issued.  Their ratio is the engine clock the tiles ran at (a
 //     measurement copy: the power limit of the part sets that clock).
-enum LaunchMode { kWhole = 0, kSegments = 1, kMixed = 2, kPersistent = 3, kTimed = 4 };
+//   kPhases: kWhole, and wave w of workgroup b writes eight 32-bit values to
+//     ((uint32_t *)ws)[8 * (NW*b + w) ..]: the shader cycles it spent in the
+//     main loop's wait for the next step's loads (W) and its barrier (B),
+//     summed over its KT K steps, and between one step's barrier and the
+//     next step's wait (R: the 128 MFMAs of a step with the fragment reads,
+//     loads and address arithmetic among them), summed over KT - 1 steps;
+//     KT; the cycles from the first step's wait to the loop's end; the last
+//     step's cycles after its barrier; one clock read's round trip; and 0
+//     (a measurement copy: the clock reads and one extra wait per step).
+enum LaunchMode { kWhole = 0, kSegments = 1, kMixed = 2, kPersistent = 3, kTimed = 4,
+                  kPhases = 5 };
 
 template <class T, int LAYOUT, int DT, int MODE>
 __global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs args) {
@@ -601,6 +671,9 @@ __global__ __launch_bounds__(T::NT) void gemm_kernel(GemmArgs args) {
       t[2] = c1;
       t[3] = r1;
     }
+  } else if constexpr (MODE == kPhases) {
+    const int p = __builtin_amdgcn_readfirstlane(xcd_position(b, args.grid, args.xcd_remap));
+    gemm_tile<T, LAYOUT, DT, false, false, true>(args, smem, args.tile_begin + p, 0, 0);
   } else if constexpr (MODE == kPersistent) {
     for (int v = b; v < args.grid; v += gridDim.x) {
       const int p = __builtin_amdgcn_readfirstlane(xcd_position(v, args.grid, args.xcd_remap));

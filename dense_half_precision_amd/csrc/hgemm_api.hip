@@ -36,6 +36,7 @@ struct KernelEntry {
   int nsb = 2;         // B stages of the LDS ring (A has one more)
   bool persistent = false;  // fn runs one workgroup per CU over all tiles
   bool timed = false;       // fn writes per-workgroup clock counters to the workspace
+  int counter_bytes = 32;   // ... this many bytes of them per workgroup
 };
 constexpr int kFixupThreads = 256;  // gemm_sk_fixup's workgroup size
 
@@ -81,6 +82,14 @@ template <int DT>
 constexpr KernelEntry pp_entry(const char *name, int group_m) {
   return KernelEntry{name, kTN, DT, PpCfg::BM, PpCfg::BN, PpCfg::BK, PpCfg::LDS, group_m, false,
                      true, &gemm_pp_kernel<DT>, nullptr, nullptr, nullptr, PpCfg::NT};
+}
+// the production kernel with per-wave main-loop phase clocks (launch mode
+// kPhases): a measurement copy; never chosen automatically
+template <class T, int LAYOUT, int DT>
+constexpr KernelEntry phases_entry(const char *name, int group_m) {
+  return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, false, true,
+                     &gemm_kernel<T, LAYOUT, DT, kPhases>, nullptr, nullptr, nullptr, T::NT,
+                     T::NSB, false, true, 32 * T::NW};
 }
 template <int DT>
 constexpr KernelEntry pp_timed_entry(const char *name, int group_m) {
@@ -180,6 +189,9 @@ const KernelEntry kTable[] = {
     timed_entry<T64, kTN, kF16>("tn_f16_64x64x64_clk", 4),
     pp_timed_entry<kF16>("tn_f16_256x256x64_pp_clk", 4),
     pp_timed_entry<kBF16>("tn_bf16_256x256x64_pp_clk", 4),
+    // production kernels with main-loop phase clocks (measurement copies)
+    phases_entry<T256, kTN, kF16>("tn_f16_256x256x64_ph", 4),
+    phases_entry<T256, kNN, kBF16>("nn_bf16_256x256x64_ph", 4),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -413,8 +425,9 @@ hgemm_status_t run(const Call &c, void *stream, const hgemm_config_t *cfg) {
   a.sk_split = 0;
   a.sk_tiles = 0;
   a.ws = nullptr;
-  if (e.timed) {  // 32 bytes of clock counters per workgroup in the workspace
-    if (c.ws == nullptr || c.ws_bytes < (size_t)tiles * 32) return HGEMM_ERR_UNSUPPORTED;
+  if (e.timed) {  // clock counters in the workspace, counter_bytes per workgroup
+    if (c.ws == nullptr || c.ws_bytes < (size_t)tiles * e.counter_bytes)
+      return HGEMM_ERR_UNSUPPORTED;
     a.ws = static_cast<float *>(c.ws);
   }
   if (plan.split == 0)

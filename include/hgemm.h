@@ -205,7 +205,16 @@ hgemm_status_t hgemm_gemm_ws(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t 
  * "_pp" kernel) writes four uint64_t
  * per workgroup b to the workspace at index 4b: shader clock and 100 MHz
  * real-time clock before the tile, then both after its stores of C are
- * issued; it needs 32 bytes per workgroup (HGEMM_ERR_UNSUPPORTED otherwise). */
+ * issued; it needs 32 bytes per workgroup (HGEMM_ERR_UNSUPPORTED otherwise).
+ * A "_ph" kernel (a measurement copy of a production kernel whose main loop
+ * reads the shader clock around each step's wait and barrier) writes eight
+ * uint32_t per wave w of workgroup b at index 8*(4b + w): the cycles the wave
+ * spent in the wait for the next step's loads and in the barrier, each summed
+ * over the K steps, the cycles between a step's barrier and the next step's
+ * wait summed over all but the last step, the number of K steps, the cycles
+ * from the first step's wait to the loop's end, the last step's cycles after
+ * its barrier, the round trip of one clock read, and a zero; it needs 128
+ * bytes per workgroup. */
 hgemm_status_t hgemm_gemm_ws_ex(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N,
                                 int64_t K, hgemm_dtype_t dtype, float alpha, const void *A, int64_t lda, const void *B,
                                 int64_t ldb, float beta, void *C, int64_t ldc, void *workspace,
@@ -252,8 +261,9 @@ int hgemm_kernel_count(void);
  * ablation changes ("_plainlds": LDS without the XOR swizzle, "_directepi":
  * epilogue without LDS staging, "_pp": eight waves in two groups alternating
  * memory and MFMA phases), and an "rs_" prefix for the register-staged
- * 32x32x16 baseline design (suffix: its LDS layout), and a "_clk" suffix for
- * measurement copies that record per-workgroup clocks (see hgemm_gemm_ws_ex).
+ * 32x32x16 baseline design (suffix: its LDS layout), and "_clk" and "_ph"
+ * suffixes for measurement copies that record per-workgroup clocks and
+ * per-wave main-loop phase cycles (see hgemm_gemm_ws_ex).
  * The integers describing
  * it are written through the non-NULL pointers: layout 0 = TN (A[M][K],
  * Bt[N][K]), 1 = NN (A[M][K], B[K][N]), 2 = at_tn (At[K][M], Bt[N][K]), 3 =

@@ -58,11 +58,12 @@ def test_edge_shapes_auto(layout, dtype):
 
 
 def _tn_nn_kernels():
-    # the "_clk" measurement copies need a counter buffer and have tests of
-    # their own (test_gpu_clock.py)
+    # the "_clk" and "_ph" measurement copies need a counter buffer and have
+    # tests of their own (test_gpu_clock.py)
     try:
         return [k["index"] for k in hgemm.kernel_table()
-                if k["layout"] in (hgemm.TN, hgemm.NN) and not k["name"].endswith("_clk")]
+                if k["layout"] in (hgemm.TN, hgemm.NN)
+                and not k["name"].endswith(("_clk", "_ph"))]
     except ImportError:  # library not built: collected as no cases
         return []
 

@@ -45,10 +45,10 @@ def _kernels_for(opA, opB, dt):
     layout = {(0, 1): hgemm.TN, (0, 0): hgemm.NN, (1, 1): hgemm.AT_TN, (1, 0): hgemm.AT_NN}[(opA, opB)]
     code = hgemm.F16 if dt == "f16" else hgemm.BF16
     # every entry but the register-staged baselines, which take packed operands,
-    # alpha 1 and beta 0 only, and the "_clk" measurement copies, which need a
-    # counter buffer (tested in test_gpu_clock.py)
+    # alpha 1 and beta 0 only, and the "_clk" and "_ph" measurement copies,
+    # which need a counter buffer (tested in test_gpu_clock.py)
     return [k for k in hgemm.kernel_table() if k["layout"] == layout and k["dtype"] == code
-            and not k["name"].startswith("rs_") and not k["name"].endswith("_clk")]
+            and not k["name"].startswith("rs_") and not k["name"].endswith(("_clk", "_ph"))]
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
