@@ -650,12 +650,14 @@ def phases(widx: int, launches: int, settle_ms: float) -> int:
     """Where the main loop's cycles go: after the settle phase, `launches`
     launches of the workload kernel's "_ph" copy, which reads the shader
     clock around each K step's wait for the next step's loads (W) and its
-    barrier (B), the rest of the step (R: 128 MFMAs, ideally 2048 cycles, with
-    the fragment reads, loads and address arithmetic among them), then as
-    many of its "_clk" copy (per-workgroup shader cycles of the unchanged
-    kernel).  One JSON line: mean cycles per step of each phase over all
-    waves, their spread over waves, and the unchanged kernel's cycles per
-    step (tile cycles / K steps, prologue and epilogue included)."""
+    barrier (B), the rest of the step (R: its MFMAs, 16 cycles each, with
+    the fragment reads, loads and address arithmetic among them; 128 MFMAs
+    for the 256 x 256 tile, 32 for 128 x 128), then as many of its "_clk"
+    copy (per-workgroup shader cycles of the unchanged kernel).  One JSON
+    line: mean cycles per step of each phase over all waves, their spread
+    over waves, the tile's start up to the first step's wait and its
+    epilogue (cycles per tile), and the unchanged kernel's cycles per step
+    (tile cycles / K steps, prologue and epilogue included)."""
     import numpy as np
     import torch
     from dense_half_precision_amd import hgemm, inputs
@@ -674,22 +676,23 @@ def phases(widx: int, launches: int, settle_ms: float) -> int:
     sp = torch.cuda.current_stream().cuda_stream
     args = (hgemm.OP_N, opB, w.M, w.N, w.K, w.dtype, 1.0, dA.data_ptr(), w.K, dB.data_ptr(), ldb,
             0.0, dC.data_ptr(), w.N)
-    ph = torch.zeros((launches, tiles, 4, 8), dtype=torch.int32, device="cuda")
+    ph = torch.zeros((launches, tiles, 4, 16), dtype=torch.int32, device="cuda")
     clk = EngineClock(w, dA, dB, dC, kname, launches=launches)
     fn = hgemm.lib().hgemm_tn if w.layout == "tn" else hgemm.lib().hgemm_nn
     largs = (w.M, w.N, w.K, hgemm.F16 if w.dtype == "f16" else hgemm.BF16, dA.data_ptr(),
              dB.data_ptr(), dC.data_ptr(), sp)
     settle(lambda: fn(*largs), settle_ms)
     for i in range(launches):
-        st = hgemm.hgemm_gemm_ws(*args, ph[i].data_ptr(), tiles * 128, sp, kernel=kph)
+        st = hgemm.hgemm_gemm_ws(*args, ph[i].data_ptr(), tiles * 256, sp, kernel=kph)
         if st != hgemm.OK:
             raise hgemm.HgemmError(st, "phase-clock launch")
     clk.enqueue()
     torch.cuda.synchronize()
-    v = ph.cpu().numpy().astype(np.int64).reshape(-1, 8)  # one row per wave
+    v = ph.cpu().numpy().astype(np.int64).reshape(-1, 16)  # one row per wave
     kt = v[:, 3]
     assert (kt == kt[0]).all() and kt[0] > 1
     KT = int(kt[0])
+    mfma_step = (info["bm"] // 32) * (info["bn"] // 32) * 2  # four waves of BM/2 x BN/2
     wait, bar, rest = v[:, 0] / KT, v[:, 1] / KT, v[:, 2] / (KT - 1)
     total = wait + bar + rest
     # the wait after c also waits for c's own result, and the wait after e
@@ -703,7 +706,7 @@ def phases(widx: int, launches: int, settle_ms: float) -> int:
                                           "barrier": round(float(bar.mean()), 1),
                                           "rest": round(float(rest.mean()), 1),
                                           "total": round(float(total.mean()), 1),
-                                          "ideal_mfma": 128 * 16},
+                                          "ideal_mfma": mfma_step * 16},
                       "p10_p50_p90_over_waves": {"wait": q(wait), "barrier": q(bar),
                                                  "rest": q(rest), "total": q(total)},
                       "clock_read_round_trip": rt,
@@ -713,6 +716,8 @@ def phases(widx: int, launches: int, settle_ms: float) -> int:
                           "rest": round(float(rest.mean()) - max(rt - 16.0, 0.0), 1),
                           "total": round(float(total.mean()) - rt - max(rt - 16.0, 0.0), 1)},
                       "last_step_after_barrier": round(float(v[:, 5].mean()), 1),
+                      "tile_start_to_first_wait": round(float(v[:, 7].mean()), 1),
+                      "epilogue": round(float(v[:, 8].mean()), 1),
                       "loop_cycles_per_step": round(float((v[:, 4] / KT).mean()), 1),
                       "unchanged_kernel_tile_cycles_per_step": round(float(tile_cyc.mean() / KT), 1),
                       "sclk_mhz": round(clk.mhz())}), flush=True)

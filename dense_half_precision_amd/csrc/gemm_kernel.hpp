@@ -165,13 +165,39 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T:
       // lines for the end of the launch to write back (measured: TN f16 8192^3
       // 740 -> 725 us, NN bf16 4096^3 98.4 -> 97.4, TN f16 2048^3 18.3 -> 18.0;
       // the same bits)
+      // The LDS reads go out in batches of up to 8 before their stores, so
+      // that their latencies overlap (one read, wait, store at a time took
+      // 9k cycles a 256 x 256 tile), and the row pointer steps by RPI rows.
+      // A wave block inside M x N stores without per-lane predicates.
       constexpr int LPR = T::WTN / 8, RPI = 64 / LPR;
+      constexpr int NROW = T::WTM / RPI, BATCH = NROW < 8 ? NROW : 8;
+      static_assert(NROW % BATCH == 0, "store batches");
+      const int row0 = lane / LPR, col = 8 * (lane % LPR);
+      const char *src = cw + row0 * T::CROW + col * 2;
+      uint16_t *dst = args.C + (size_t)(wm0 + row0) * ldc + (wn0 + col);
+      const size_t step = (size_t)RPI * ldc;
+      const bool inside = wm0 + T::WTM <= M && wn0 + T::WTN <= N;  // uniform
+      const int rows_left = M - wm0 - row0;  // this lane's rows: r * RPI < rows_left
+      const bool col_in = wn0 + col < N;
 #pragma unroll
-      for (int r = 0; r < T::WTM / RPI; ++r) {
-        const int row = r * RPI + lane / LPR, col = 8 * (lane % LPR);
-        const u32x4 v = *(const u32x4 *)(cw + row * T::CROW + col * 2);
-        const int m = wm0 + row, n = wn0 + col;
-        if (m < M && n < N) __builtin_nontemporal_store(v, (u32x4 *)(args.C + (size_t)m * ldc + n));
+      for (int r0 = 0; r0 < NROW; r0 += BATCH) {
+        u32x4 v[BATCH];
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b)
+          v[b] = *(const u32x4 *)(src + (r0 + b) * RPI * T::CROW);
+        if (inside) {
+#pragma unroll
+          for (int b = 0; b < BATCH; ++b) {
+            __builtin_nontemporal_store(v[b], (u32x4 *)dst);
+            dst += step;
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < BATCH; ++b) {
+            if (col_in && (r0 + b) * RPI < rows_left) __builtin_nontemporal_store(v[b], (u32x4 *)dst);
+            dst += step;
+          }
+        }
       }
     } else {
 #pragma unroll
@@ -200,8 +226,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T:
 // workspace slot `slot` (a separate instantiation, so that whole-K tiles
 // carry none of the segment bookkeeping in registers).
 // PH: a measurement copy that reads the shader clock (s_memtime) at three
-// points of every K step and writes each wave's per-phase cycle sums to
-// ((uint32_t *)args.ws)[8 * (NW * blockIdx.x + wave) ..] (see the main loop).
+// points of every K step, and at the tile's start and end, and writes each
+// wave's per-phase cycle sums to ((uint32_t *)args.ws)[16 * (NW * blockIdx.x
+// + wave) ..] (see the main loop and the kPhases launch mode).
 template <class T, int LAYOUT, int DT, bool SPLIT, bool OPAQUE = false, bool PH = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int tile, int seg,
                                           int slot) {
@@ -221,6 +248,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   constexpr bool A_FIRST = A_MN && !B_MN;
   constexpr bool ALL_TR = A_MN && B_MN;
 
+  // (PH) the tile's start, retired by the prologue's wait
+  uint32_t ph_start = 0;
+  if constexpr (PH) ph_start = (uint32_t)__builtin_amdgcn_s_memtime();
   const int M = args.M, N = args.N;
   const int lda = args.lda, ldb = args.ldb;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -479,6 +509,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   //       reads, loads and address arithmetic among them (KT - 1 of these).
   uint32_t ph_w = 0, ph_b = 0, ph_r = 0;
   uint32_t pc = 0, pd = 0, pe = 0, ph_first = 0;
+  uint32_t ph_out[9];
   auto stamp = [&]() { return (uint32_t)__builtin_amdgcn_s_memtime(); };
 
   // ---- main loop -------------------------------------------------------------
@@ -571,17 +602,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     const uint32_t rt1 = stamp();
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-    if (lane == 0) {
-      uint32_t *o = reinterpret_cast<uint32_t *>(args.ws) + 8 * ((size_t)T::NW * blockIdx.x + wave);
-      o[0] = ph_w;
-      o[1] = ph_b;
-      o[2] = ph_r;
-      o[3] = (uint32_t)KT;
-      o[4] = KT > 0 ? end - ph_first : 0u;  // first step's c to the loop's end
-      o[5] = KT > 0 ? end - pe : 0u;        // the last step's Z
-      o[6] = rt1 - rt0;
-      o[7] = 0;
-    }
+    ph_out[0] = ph_w;
+    ph_out[1] = ph_b;
+    ph_out[2] = ph_r;
+    ph_out[3] = (uint32_t)KT;
+    ph_out[4] = KT > 0 ? end - ph_first : 0u;  // first step's c to the loop's end
+    ph_out[5] = KT > 0 ? end - pe : 0u;        // the last step's Z
+    ph_out[6] = rt1 - rt0;
+    ph_out[7] = KT > 0 ? ph_first - ph_start : 0u;  // tile start to the first step's c
+    ph_out[8] = rt1;  // where the epilogue starts
   }
 
   // The last step (or, for K = 0, the prologue) read fragments for a step that
@@ -618,6 +647,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   } else {
     store_tile<T, DT>(args, acc, smem, m0, n0, wave, lane);
   }
+  if constexpr (PH) {
+    const uint32_t done = (uint32_t)__builtin_amdgcn_s_memtime();
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    if (lane == 0) {
+      uint32_t *o = reinterpret_cast<uint32_t *>(args.ws) + 16 * ((size_t)T::NW * blockIdx.x + wave);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = ph_out[i];
+      o[8] = done - ph_out[8];  // the epilogue, up to its stores of C issued
+#pragma unroll
+      for (int i = 9; i < 16; ++i) o[i] = 0;
+    }
+  }
 }
 
 // Launch modes (the position of a workgroup is its index after the XCD remap
@@ -640,15 +681,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
 //     real-time clock (s_memrealtime) before its tile and after its stores
 //     of C are issued.  Their ratio is the engine clock the tiles ran at (a
 //     measurement copy: the power limit of the part sets that clock).
-//   kPhases: kWhole, and wave w of workgroup b writes eight 32-bit values to
-//     ((uint32_t *)ws)[8 * (NW*b + w) ..]: the shader cycles it spent in the
-//     main loop's wait for the next step's loads (W) and its barrier (B),
-//     summed over its KT K steps, and between one step's barrier and the
-//     next step's wait (R: the 128 MFMAs of a step with the fragment reads,
-//     loads and address arithmetic among them), summed over KT - 1 steps;
-//     KT; the cycles from the first step's wait to the loop's end; the last
-//     step's cycles after its barrier; one clock read's round trip; and 0
-//     (a measurement copy: the clock reads and one extra wait per step).
+//   kPhases: kWhole, and wave w of workgroup b writes sixteen 32-bit values
+//     to ((uint32_t *)ws)[16 * (NW*b + w) ..]: the shader cycles it spent in
+//     the main loop's wait for the next step's loads (W) and its barrier
+//     (B), summed over its KT K steps, and between one step's barrier and
+//     the next step's wait (R: a step's MFMAs with the fragment reads, loads
+//     and address arithmetic among them), summed over KT - 1 steps; KT; the
+//     cycles from the first step's wait to the loop's end; the last step's
+//     cycles after its barrier; one clock read's round trip; the cycles from
+//     the tile's start to the first step's wait (the prologue and the first
+//     step's MFMAs before its wait); the epilogue's cycles up to its stores
+//     of C issued; and seven 0s (a measurement copy: the clock reads and one
+//     extra wait per step).
 enum LaunchMode { kWhole = 0, kSegments = 1, kMixed = 2, kPersistent = 3, kTimed = 4,
                   kPhases = 5 };
 

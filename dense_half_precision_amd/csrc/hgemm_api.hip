@@ -89,7 +89,7 @@ template <class T, int LAYOUT, int DT>
 constexpr KernelEntry phases_entry(const char *name, int group_m) {
   return KernelEntry{name, LAYOUT, DT, T::BM, T::BN, T::BK, T::LDS, group_m, false, true,
                      &gemm_kernel<T, LAYOUT, DT, kPhases>, nullptr, nullptr, nullptr, T::NT,
-                     T::NSB, false, true, 32 * T::NW};
+                     T::NSB, false, true, 64 * T::NW};
 }
 template <int DT>
 constexpr KernelEntry pp_timed_entry(const char *name, int group_m) {
@@ -192,6 +192,7 @@ const KernelEntry kTable[] = {
     // production kernels with main-loop phase clocks (measurement copies)
     phases_entry<T256, kTN, kF16>("tn_f16_256x256x64_ph", 4),
     phases_entry<T256, kNN, kBF16>("nn_bf16_256x256x64_ph", 4),
+    phases_entry<T128R3, kTN, kF16>("tn_f16_128x128x64_r3_ph", 4),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 

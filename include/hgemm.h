@@ -207,14 +207,15 @@ hgemm_status_t hgemm_gemm_ws(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t 
  * real-time clock before the tile, then both after its stores of C are
  * issued; it needs 32 bytes per workgroup (HGEMM_ERR_UNSUPPORTED otherwise).
  * A "_ph" kernel (a measurement copy of a production kernel whose main loop
- * reads the shader clock around each step's wait and barrier) writes eight
- * uint32_t per wave w of workgroup b at index 8*(4b + w): the cycles the wave
- * spent in the wait for the next step's loads and in the barrier, each summed
- * over the K steps, the cycles between a step's barrier and the next step's
- * wait summed over all but the last step, the number of K steps, the cycles
- * from the first step's wait to the loop's end, the last step's cycles after
- * its barrier, the round trip of one clock read, and a zero; it needs 128
- * bytes per workgroup. */
+ * reads the shader clock around each step's wait and barrier) writes sixteen
+ * uint32_t per wave w of workgroup b at index 16*(4b + w): the cycles the
+ * wave spent in the wait for the next step's loads and in the barrier, each
+ * summed over the K steps, the cycles between a step's barrier and the next
+ * step's wait summed over all but the last step, the number of K steps, the
+ * cycles from the first step's wait to the loop's end, the last step's cycles
+ * after its barrier, the round trip of one clock read, the cycles from the
+ * tile's start to the first step's wait, the epilogue's cycles up to its
+ * stores of C issued, and seven zeros; it needs 256 bytes per workgroup. */
 hgemm_status_t hgemm_gemm_ws_ex(hgemm_op_t opA, hgemm_op_t opB, int64_t M, int64_t N,
                                 int64_t K, hgemm_dtype_t dtype, float alpha, const void *A, int64_t lda, const void *B,
                                 int64_t ldb, float beta, void *C, int64_t ldc, void *workspace,

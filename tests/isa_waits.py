@@ -164,5 +164,18 @@ _ACC_STORE = re.compile(r"global_store_dwordx4 v\[\d+:\d+\], (a\[\d+:\d+\]), off
 
 def acc_store_sources(lines) -> list:
     """The accumulator registers each partial-sum store (inline assembly,
-    storing straight from AGPRs) reads, in order."""
-    return [m.group(1) for l in lines for m in [_ACC_STORE.search(l.split(";")[0])] if m]
+    storing straight from AGPRs) reads, in order.  Only stores inside inline
+    assembly count (between the compiler's ;;#ASMSTART and ;;#ASMEND
+    markers): a store the compiler emits itself from accumulator registers is
+    padded by the compiler and may reuse its registers."""
+    out, in_asm = [], False
+    for l in lines:
+        if ";;#ASMSTART" in l:
+            in_asm = True
+        elif ";;#ASMEND" in l:
+            in_asm = False
+        elif in_asm:
+            m = _ACC_STORE.search(l.split(";")[0])
+            if m:
+                out.append(m.group(1))
+    return out

@@ -51,6 +51,7 @@ def test_clock_copy_matches_production(name, layout, dtype, shape):
 @pytest.mark.parametrize("name,layout,dtype,shape", [
     ("tn_f16_256x256x64", "tn", "f16", (520, 776, 1000)),
     ("nn_bf16_256x256x64", "nn", "bf16", (300, 512, 136)),
+    ("tn_f16_128x128x64_r3", "tn", "f16", (264, 392, 1608)),
 ])
 def test_phase_copy_matches_production(name, layout, dtype, shape):
     """The "_ph" copies: the same C as the production kernel bit for bit, and
@@ -65,22 +66,25 @@ def test_phase_copy_matches_production(name, layout, dtype, shape):
     k = hgemm.kernel_index(name + "_ph")
     info = hgemm.kernel_table()[k]
     tiles = -(-M // info["bm"]) * -(-N // info["bn"])
-    ph = torch.zeros((tiles, 4, 8), dtype=torch.int32, device="cuda")
+    ph = torch.zeros((tiles, 4, 16), dtype=torch.int32, device="cuda")
     dA, dB = helpers.to_dev(A), helpers.to_dev(B)
     dC = helpers.empty_dev(M, N)
     opB = hgemm.OP_T if layout == "tn" else hgemm.OP_N
     ldb = K if layout == "tn" else N
     args = (hgemm.OP_N, opB, M, N, K, dtype, 1.0, dA.data_ptr(), K, dB.data_ptr(), ldb, 0.0,
             dC.data_ptr(), N)
-    assert hgemm.hgemm_gemm_ws(*args, ph.data_ptr(), tiles * 128 - 1, helpers.stream_ptr(),
+    assert hgemm.hgemm_gemm_ws(*args, ph.data_ptr(), tiles * 256 - 1, helpers.stream_ptr(),
                                kernel=k) == hgemm.ERR_UNSUPPORTED
-    assert hgemm.hgemm_gemm_ws(*args, ph.data_ptr(), tiles * 128, helpers.stream_ptr(),
+    assert hgemm.hgemm_gemm_ws(*args, ph.data_ptr(), tiles * 256, helpers.stream_ptr(),
                                kernel=k) == hgemm.OK
     assert np.array_equal(helpers.to_host(dC), want)
-    v = ph.cpu().numpy().astype(np.int64).reshape(-1, 8)
+    v = ph.cpu().numpy().astype(np.int64).reshape(-1, 16)
     kt = -(-K // 64)
     assert (v[:, 3] == kt).all()
     assert (v[:, 0:3] >= 0).all() and (v[:, 2] > 0).all()
     assert (v[:, 0] + v[:, 1] + v[:, 2] + v[:, 5] <= v[:, 4] + 64).all(), "phases exceed the loop"
-    assert (v[:, 2] >= (kt - 1) * 128 * 16 * 0.9).all(), "fewer cycles than the MFMAs need"
+    mfma_step = (info["bm"] // 32) * (info["bn"] // 32) * 2
+    assert (v[:, 2] >= (kt - 1) * mfma_step * 16 * 0.9).all(), "fewer cycles than the MFMAs need"
     assert ((v[:, 6] > 0) & (v[:, 6] < 2000)).all(), "clock read round trip"
+    assert (v[:, 7] > 0).all() and (v[:, 8] > 0).all(), "prologue and epilogue"
+    assert (v[:, 9:] == 0).all()
