@@ -432,6 +432,111 @@ def tail() -> int:
     return 0
 
 
+# TN f16 shapes of the automatic-choice sweep: squares, other K depths,
+# skinny and ragged shapes.
+SWEEP_SHAPES = ([(s, s, s) for s in (512, 768, 1024, 1536, 2048, 2560, 3072, 3584, 4096, 5120,
+                                    6144, 7168, 8192)]
+                + [(4096, 4096, 256), (4096, 4096, 1024), (4096, 4096, 16384), (2048, 2048, 8192),
+                   (2048, 2048, 32768), (1024, 1024, 16384), (512, 512, 65536)]
+                + [(1024, 8192, 8192), (8192, 1024, 8192), (256, 16384, 4096), (16384, 256, 4096),
+                   (2048, 16384, 2048), (16384, 2048, 2048), (8192, 8192, 512)]
+                + [(1000, 1000, 1000), (3000, 5000, 2000), (4000, 4000, 4000), (6000, 6000, 3000),
+                   (8000, 8000, 8000)])
+# A second set, for checking the cost model on shapes it was not tuned on:
+# other TN sizes and NN bf16.
+SWEEP_CHECK = ([("tn", "f16", s, s, s) for s in (2304, 2816, 3328, 3840, 4608)]
+               + [("tn", "f16", 5632, 5632, 2816), ("tn", "f16", 7000, 5000, 4000),
+                  ("tn", "f16", 12288, 12288, 2048), ("tn", "f16", 1536, 12288, 4096),
+                  ("tn", "f16", 2560, 8192, 4096)]
+               + [("nn", "bf16", s, s, s) for s in (2048, 2560, 3072, 4096, 6144)]
+               + [("nn", "bf16", 1024, 8192, 8192), ("nn", "bf16", 6000, 6000, 3000)])
+SWEEP_TILES = ("256x256x64", "128x128x64_r3", "128x128x64", "64x64x64")
+
+
+def sweep(which: str = "tn") -> int:
+    """The automatic choice against every production kernel (and the K split
+    of the tail, given a workspace) over SWEEP_SHAPES, TN f16, operands uniform
+    in [-1, 1].  Per shape, every candidate runs back to back between one pair
+    of events, queued behind a QueueHold launch, in three alternating rounds
+    (median).  One JSON line per shape: TFLOPS of each candidate (with a
+    workspace, hgemm_gemm_ws runs the K split of the tail where its cost
+    model expects a gain), the automatic choice without a workspace, and how
+    far it, and the call with a workspace, fall behind the best candidate; a
+    summary line at the end.  `which`: "tn" (SWEEP_SHAPES) or "check"
+    (SWEEP_CHECK)."""
+    import numpy as np
+    import torch
+    from dense_half_precision_amd import hgemm
+    sp = torch.cuda.current_stream().cuda_stream
+    hold = QueueHold()
+    regrets, regrets_ws = [], []
+    shapes = ([("tn", "f16", M, N, K) for M, N, K in SWEEP_SHAPES] if which == "tn"
+              else SWEEP_CHECK)
+    for lay, dt, M, N, K in shapes:
+        g = torch.Generator(device="cuda").manual_seed(M * 131 + N * 17 + K)
+        tdt = torch.float16 if dt == "f16" else torch.bfloat16
+        dA = (torch.rand((M, K), device="cuda", generator=g) * 2 - 1).to(tdt)
+        dB = (torch.rand((N, K) if lay == "tn" else (K, N), device="cuda", generator=g) * 2 - 1).to(tdt)
+        dC = torch.empty((M, N), dtype=tdt, device="cuda")
+        opB, ldb = (hgemm.OP_T, K) if lay == "tn" else (hgemm.OP_N, N)
+        args = (hgemm.OP_N, opB, M, N, K, dt, 1.0, dA.data_ptr(), K, dB.data_ptr(), ldb,
+                0.0, dC.data_ptr(), N)
+        need = hgemm.gemm_ws_size(hgemm.OP_N, opB, M, N, K, dt)
+        ws = torch.empty(max(need, 16) // 4, dtype=torch.float32, device="cuda")
+        fn = hgemm.hgemm_tn_ex if lay == "tn" else hgemm.hgemm_nn_ex
+        cands = {name: (lambda k=hgemm.kernel_index(name): fn(
+                            M, N, K, dt, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), sp, kernel=k))
+                 for name in (f"{lay}_{dt}_{t}" for t in SWEEP_TILES)}
+        if need > 0:  # hgemm_gemm_ws: the K split of the tail where it estimates it faster
+            cands["auto with workspace"] = lambda: hgemm.hgemm_gemm_ws(
+                *args, ws.data_ptr(), need, sp)
+        auto = hgemm.kernel_table()[hgemm.auto_kernel(hgemm.TN if lay == "tn" else hgemm.NN,
+                                                      dt, M, N, K)]["name"]
+        flop = 2.0 * M * N * K
+        n = int(min(200, max(5, 20e-3 / (flop / 1.0e15))))  # about 20 ms a run
+        times = {k: [] for k in cands}
+        for f in cands.values():
+            for _ in range(3):
+                if f() != hgemm.OK:
+                    raise hgemm.HgemmError(hgemm.ERR_INVALID_ARG, "sweep launch")
+        torch.cuda.synchronize()
+        for _ in range(3):
+            for name, f in cands.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                hold.hold(n * 0.03)
+                e0.record()
+                for _ in range(n):
+                    f()
+                e1.record()
+                torch.cuda.synchronize()
+                times[name].append(e0.elapsed_time(e1) / n)
+        ms = {k: float(np.median(v)) for k, v in times.items()}
+        # without a workspace the candidates are the kernels; with one, also
+        # what hgemm_gemm_ws runs
+        best = min((k for k in ms if k != "auto with workspace"), key=ms.get)
+        r = ms[auto] / ms[best] - 1.0
+        regrets.append(r)
+        line = {"sweep": f"{lay} {dt} {M}x{N}x{K}", "tflops": {k: round(flop / v / 1e9, 1) for k, v in ms.items()},
+                "auto": auto, "best_kernel": best, "auto_behind_best_kernel_pct": round(100 * r, 1)}
+        if need > 0:
+            best_all = min(ms.values())
+            rws = ms["auto with workspace"] / best_all - 1.0
+            regrets_ws.append(rws)
+            line["with_workspace_behind_best_pct"] = round(100 * rws, 1)
+            line["with_workspace_ahead_of_auto_pct"] = round(100 * (ms[auto] / ms["auto with workspace"] - 1), 1)
+        print(json.dumps(line), flush=True)
+        del dA, dB, dC, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep_summary": which, "shapes": len(shapes),
+                      "auto_behind_best_kernel_pct_mean": round(100 * float(np.mean(regrets)), 2),
+                      "auto_behind_best_kernel_pct_max": round(100 * float(np.max(regrets)), 1),
+                      "shapes_within_2pct": int(sum(r <= 0.02 for r in regrets)),
+                      "with_workspace_shapes": len(regrets_ws),
+                      "with_workspace_within_2pct_of_best": int(sum(r <= 0.02 for r in regrets_ws))}),
+          flush=True)
+    return 0
+
+
 class EngineClock:
     """Engine clock a kernel runs at, from its measurement copy (the "_clk"
     twin of the same kernel, which writes the shader clock and the 100 MHz
@@ -822,6 +927,9 @@ def main() -> int:
     ap.add_argument("--clock-trace", type=int, default=0, metavar="LAUNCHES",
                     help="print the engine clock over this many back-to-back launches of the "
                          "workload's kernel after 2 s idle, and exit")
+    ap.add_argument("--sweep", choices=("tn", "check"), default=None,
+                    help="the automatic choice against every production kernel over a grid of "
+                         "TN f16 shapes ('tn') or a second set with NN bf16 ('check'), and exit")
     ap.add_argument("--phases", type=int, default=0, metavar="LAUNCHES",
                     help="after the settle phase, time the main loop's phases (wait, barrier, "
                          "rest) with the workload kernel's '_ph' copy over this many launches, "
@@ -842,6 +950,11 @@ def main() -> int:
             print("bench.py: one GPU only", file=sys.stderr)
             return 2
         return clock_trace(args.workload, args.clock_trace)
+    if args.sweep:
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            return 2
+        return sweep(args.sweep)
     if args.phases > 0:
         if args.gpus != 1:
             print("bench.py: one GPU only", file=sys.stderr)

@@ -220,10 +220,18 @@ int find_kernel(int layout, int dtype, int bm, int nsb = 2) {
 // tile taking (KT + kTileFixed) * (t/256)^2 / rate_t units, rate_t the per-CU
 // throughput of that tile size relative to the 256 kernel.  The constants were
 // chosen on measured times of every tile size and split over square, skinny
-// and long-K shapes.
+// and long-K shapes.  The 128 x 128 and 64 x 64 kernels have two rates each:
+// one workgroup per CU (a single round; where the deeper-ring 128 variant
+// runs), and several sharing a CU when there are more tiles than CUs (two of
+// 128 x 128, four of 64 x 64, as their LDS allows).  Sweeps over 49 TN f16
+// and NN bf16 shapes put the shared rates at 0.58-0.70 and 0.25-0.45: with
+// the single-round rates there, the choice took the 128 tile where the 256
+// tile was 14-24 % faster (3072^3, 6000 x 6000 x 3000) and the 64 tile where
+// the 128 tile was 30 % faster (2304^3).
 constexpr int64_t kCUs = 256;
 const int kSizes[3] = {256, 128, 64};
 const double kRate[3] = {1.0, 0.8, 0.5};  // sustained rate relative to the 256 x 256 tile
+const double kRateShared[3] = {1.0, 0.64, 0.37};  // ... with more tiles than CUs
 constexpr double kTileFixed = 3.0;        // prologue and epilogue of a tile, in K steps
 constexpr double kSplitFixed = 6.9;       // the fixup launch and the wait for it
 constexpr double kSlotCost = 0.055;       // one 256 KiB partial sum written and read back
@@ -233,8 +241,9 @@ constexpr int64_t kMaxSlots = 1024;       // 256 MiB of partial sums at most
 double dp_cost(int i, int64_t M, int64_t N, int64_t KT) {
   const int64_t t = kSizes[i];
   const int64_t tiles = ((M + t - 1) / t) * ((N + t - 1) / t);
+  const double rate = tiles > kCUs ? kRateShared[i] : kRate[i];
   return (double)((tiles + kCUs - 1) / kCUs) * ((double)KT + kTileFixed) * (double)(t * t) /
-         65536.0 / kRate[i];
+         65536.0 / rate;
 }
 
 // Automatic choice without a K split: the tile size with the least estimated

@@ -202,6 +202,15 @@ def test_kernel_table_and_auto_choice():
     assert tab[hgemm.auto_kernel(3, 1, 1536, 1536, 1536)]["name"] == "at_nn_bf16_128x128x64_r3"
     assert tab[hgemm.auto_kernel(1, 1, 2048, 2048, 1472)]["name"] == "nn_bf16_128x128x64"
     assert tab[hgemm.auto_kernel(0, 0, 1024, 8192, 8192)]["name"] == "tn_f16_128x128x64"
+    # tiles that share CUs (more tiles than CUs) run at the measured shared
+    # rates: 3072^3 and 6000 x 6000 x 3000 take the 256 x 256 tile (14 % and 24 %
+    # faster there than 128 x 128), 2560^3 and 2304^3 the 128 x 128 one (26 %
+    # and 30 % faster there than the 256 and 64 tiles), 1024^3 still 64 x 64
+    assert tab[hgemm.auto_kernel(0, 0, 3072, 3072, 3072)]["bm"] == 256
+    assert tab[hgemm.auto_kernel(0, 0, 6000, 6000, 3000)]["bm"] == 256
+    assert tab[hgemm.auto_kernel(0, 0, 2560, 2560, 2560)]["name"] == "tn_f16_128x128x64"
+    assert tab[hgemm.auto_kernel(0, 0, 2304, 2304, 2304)]["name"] == "tn_f16_128x128x64"
+    assert tab[hgemm.auto_kernel(0, 0, 1024, 1024, 1024)]["bm"] == 64
 
 
 @pytest.mark.parametrize("tiles_m,tiles_n", [(1, 1), (2, 2), (3, 5), (32, 32), (16, 16), (8, 8),
