@@ -83,6 +83,14 @@ constexpr KernelEntry pp_entry(const char *name, int group_m) {
   return KernelEntry{name, kTN, DT, PpCfg::BM, PpCfg::BN, PpCfg::BK, PpCfg::LDS, group_m, false,
                      true, &gemm_pp_kernel<DT>, nullptr, nullptr, nullptr, PpCfg::NT};
 }
+// the 128 x 128 tile on eight waves in two groups that split K: leading
+// dimensions, alpha and beta, no K split; an ablation, never chosen
+// automatically
+template <int DT>
+constexpr KernelEntry ppk_entry(const char *name, int group_m) {
+  return KernelEntry{name, kTN, DT, PpkCfg::BM, PpkCfg::BN, PpkCfg::BK, PpkCfg::LDS, group_m,
+                     false, true, &gemm_ppk_kernel<DT>, nullptr, nullptr, nullptr, PpkCfg::NT};
+}
 // the production kernel with per-wave main-loop phase clocks (launch mode
 // kPhases): a measurement copy; never chosen automatically
 template <class T, int LAYOUT, int DT>
@@ -193,6 +201,9 @@ const KernelEntry kTable[] = {
     phases_entry<T256, kTN, kF16>("tn_f16_256x256x64_ph", 4),
     phases_entry<T256, kNN, kBF16>("nn_bf16_256x256x64_ph", 4),
     phases_entry<T128R3, kTN, kF16>("tn_f16_128x128x64_r3_ph", 4),
+    // the 128 x 128 tile on eight waves in two groups that split K (TN)
+    ppk_entry<kF16>("tn_f16_128x128x64_ppk", 4),
+    ppk_entry<kBF16>("tn_bf16_128x128x64_ppk", 4),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
