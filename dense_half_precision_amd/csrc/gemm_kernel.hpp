@@ -22,7 +22,9 @@
 // + 1 A stages and NSB B stages, three and two for a 256 x 256 tile (A and B
 // of one K step of 64 are 32 KiB each there, 160 KiB in all): the loads of
 // step s are issued during step s - NSB, those of A before that step's
-// barrier and those of B after it -- the multi-stage pipeline of the HGEMM MMA note and
+// barrier and those of B after it (the SPREAD configurations: NSB A and NSB B
+// stages, both loaded during step s - NSB + 1, evenly among the MFMAs before
+// its barrier) -- the multi-stage pipeline of the HGEMM MMA note and
 // of the tcgen05 translation's pipelining section, sized to the 160 KiB LDS of
 // gfx950.  Each 128-byte row of a K step is stored with its
 // 16-byte chunks XOR-swizzled (chunk ^ ((row >> 1) & 7)), an LDS layout that
@@ -69,13 +71,16 @@
 namespace hgemm {
 
 template <int BM_, int BN_, int LDS_ = kLdsXor, int EPI_ = 1, int WVM_ = 2, int WVN_ = 2,
-          int NSB_ = 2>
+          int NSB_ = 2, int SPREAD_ = 0>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 64;
   static constexpr int WVM = WVM_, WVN = WVN_;        // waves along M and N
-  // LDS ring: NSA stages of A and NSB of B; A is loaded NSA - 1 steps ahead
-  // (in slice 0), B NSB steps ahead (after the barrier)
-  static constexpr int NSB = NSB_, NSA = NSB_ + 1;
+  // LDS ring: NSA stages of A and NSB of B.  SPREAD 0: A is loaded NSA - 1
+  // steps ahead (in slice 0), B NSB steps ahead (after the barrier), NSA =
+  // NSB + 1.  SPREAD 1: both are loaded NSB - 1 steps ahead, spread evenly
+  // over the step's MFMAs before the barrier, NSA = NSB.
+  static constexpr int SPREAD = SPREAD_;
+  static constexpr int NSB = NSB_, NSA = SPREAD_ ? NSB_ : NSB_ + 1;
   static constexpr int NW = WVM * WVN;                // waves per workgroup
   static constexpr int NT = 64 * NW;
   static constexpr int WTM = BM / WVM, WTN = BN / WVN;  // wave block
@@ -99,6 +104,7 @@ struct TileCfg {
   static_assert(FM % 2 == 0, "the slice is split in halves by A block");
   static_assert(LDS_BYTES <= 163840, "160 KiB of LDS");
   static_assert(LDS == kLdsXor || LDS == kLdsPlain, "layouts of this kernel");
+  static_assert(!SPREAD || NSB >= 3, "the spread loads need two steps of lead");
 };
 
 // Epilogue of a BM x BN tile whose FP32 sums a workgroup holds in acc (wave
@@ -331,10 +337,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   constexpr int NSA = T::NSA, NSB = T::NSB;
   auto a_base = [&](int s) { return (uint32_t)((s % NSA) * T::A_STAGE); };
   auto b_base = [&](int s) { return (uint32_t)(T::B_BASE + (s % NSB) * T::B_STAGE); };
-  // Loads still in flight at each step's barrier: those issued after the B
-  // loads of step kt+1 (A of NSB-1 later steps, B of NSB-2), which the wait
-  // there lets run on.
-  constexpr int AHEAD = (NSB - 1) * SEG_A + (NSB - 2) * SEG_B;
+  // Loads still in flight at each step's barrier: those issued after the
+  // loads of step kt+1 (A of NSB-1 later steps, B of NSB-2; spread: A and B
+  // of NSB-2 later steps), which the wait there lets run on.
+  constexpr bool SPREAD = T::SPREAD != 0;
+  constexpr int AHEAD = SPREAD ? (NSB - 2) * (SEG_A + SEG_B) : (NSB - 1) * SEG_A + (NSB - 2) * SEG_B;
   static_assert(AHEAD < 64, "vmcnt range");
 
   // Buffer resource of one operand for the K step starting at k0: rows past
@@ -472,14 +479,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
 
   // ---- prologue: the loads the loop's earlier steps would have issued, in
   // the same order (A of step s, then B of step s, for s = 0 .. NSB-1), the
-  // last B after the first barrier, where it overlaps the reads of slice 0 ----
+  // last B after the first barrier, where it overlaps the reads of slice 0
+  // (spread: steps 0 .. NSB-2, all before the barrier) ----
+  constexpr int LEAD = SPREAD ? NSB - 1 : NSB;  // steps loaded ahead of the loop
 #pragma unroll
-  for (int st = 0; st < NSB; ++st) {
+  for (int st = 0; st < LEAD; ++st) {
     if (tail == st) mask_tail();
     prep_a(st);
 #pragma unroll
     for (int i = 0; i < SEG_A; ++i) load_a(a_base(st), i);
-    if (st < NSB - 1) {
+    if (SPREAD || st < NSB - 1) {
       prep_b(st);
 #pragma unroll
       for (int i = 0; i < SEG_B; ++i) load_b(b_base(st), i);
@@ -487,11 +496,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(AHEAD, 0));  // step 0 in LDS
   wg_barrier();
-  prep_b(NSB - 1);
+  if constexpr (!SPREAD) prep_b(NSB - 1);
 #pragma unroll
   for (int q = 0; q < NR; ++q) {
     read_op(I0{}, a_base(0), b_base(0), 0, q);
-    if (q * SEG_B / NR != (q + 1) * SEG_B / NR) load_b(b_base(NSB - 1), q * SEG_B / NR);
+    if constexpr (!SPREAD) {
+      if (q * SEG_B / NR != (q + 1) * SEG_B / NR) load_b(b_base(NSB - 1), q * SEG_B / NR);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -520,20 +531,39 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   for (int i = 0; i < NSA; ++i) ra[i] = a_base(i);
 #pragma unroll
   for (int i = 0; i < NSB; ++i) rb[i] = b_base(i);
+  // Spread loads: the SEG_A + SEG_B loads of a step (A, then B) go after
+  // MFMAs spread_pos(0), spread_pos(1), ... of the step's first NMF + NMF/2
+  // (X and Y below), evenly spaced.
+  constexpr int SP_MF = NMF + NMF / 2, SP_LD = SEG_A + SEG_B;
+  auto spread_load = [&](int pos, uint32_t la, uint32_t lb) {
+#pragma unroll
+    for (int g = 0; g < SP_LD; ++g) {
+      if (g * SP_MF / SP_LD + SP_MF / SP_LD / 2 == pos) {
+        if (g < SEG_A) load_a(la, g);
+        else load_b(lb, g - SEG_A);
+      }
+    }
+  };
   for (int kt = 0; kt < KT; ++kt) {
-    if (__builtin_expect(kt + NSB == tail, 0)) mask_tail();  // loads of steps kt+NSB on are issued below
+    // loads of steps kt+LEAD on are issued below
+    if (__builtin_expect(kt + LEAD == tail, 0)) mask_tail();
     const uint32_t ca = ra[0], cb = rb[0];
     const uint32_t na = ra[1], nb = rb[1];
-    // X: slice 0; read slice 1; A of step kt+NSA-1 into the stage step kt-1 used
+    // X: slice 0; read slice 1; A of step kt+NSA-1 into the stage step kt-1
+    // used (spread: A and B of step kt+NSB-1, in X and Y)
     prep_a(kt + NSA - 1);
     const uint32_t la = ra[NSA - 1];
+    if constexpr (SPREAD) prep_b(kt + NSB - 1);
+    const uint32_t lb_x = rb[NSB - 1];
     wait_set(I0{});
 #pragma unroll
     for (int t = 0; t < NMF; ++t) {
       mfma(I0{}, t);
 #pragma unroll
       for (int q = t * NR / NMF; q < (t + 1) * NR / NMF; ++q) read_op(I1{}, ca, cb, 1, q);
-      if constexpr (SEG_A > 0) {
+      if constexpr (SPREAD) {
+        spread_load(t, la, lb_x);
+      } else if constexpr (SEG_A > 0) {
         constexpr int SP = NMF / SEG_A;  // one A load every SP MFMAs, after MFMA 2 mod SP
         if (t % SP == (SP > 2 ? 2 : 0)) load_a(la, t / SP);
       }
@@ -544,6 +574,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
 #pragma unroll
     for (int t = 0; t < NMF / 2; ++t) {
       mfma(I1{}, t);
+      if constexpr (SPREAD) spread_load(NMF + t, la, lb_x);
       __builtin_amdgcn_sched_barrier(0);
     }
     // step kt+1 complete in LDS (later steps' loads may stay in flight), own
@@ -560,7 +591,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
       wg_barrier();
     }
     // Z: second half of slice 1; read slice 0 of step kt+1; B of step kt+NSB
-    prep_b(kt + NSB);
+    // (spread: no loads)
+    if constexpr (!SPREAD) prep_b(kt + NSB);
     const uint32_t lb = rb[0];  // step kt+NSB reuses the B stage of step kt
 #pragma unroll
     for (int t = NMF / 2; t < NMF; ++t) {
@@ -577,7 +609,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
       const int u = t - H;
 #pragma unroll
       for (int q = u * NR / H; q < (u + 1) * NR / H; ++q) read_op(I0{}, na, nb, 0, q);
-      if constexpr (SEG_B > 0) {
+      if constexpr (SEG_B > 0 && !SPREAD) {
         constexpr int SP = H / SEG_B > 0 ? H / SEG_B : 1;
         if (u % SP == (SP > 1 ? 1 : 0) && u / SP < SEG_B) load_b(lb, u / SP);
       }

@@ -119,6 +119,9 @@ using T128x256 = TileCfg<128, 256>;
 using W128x256 = WsCfg<128, 256>;
 using T256W2x4 = TileCfg<256, 256, kLdsXor, 1, 2, 4>;  // eight waves, two per SIMD
 using T128R3 = TileCfg<128, 128, kLdsXor, 1, 2, 2, 3>;  // 4 A + 3 B stages, 112 KiB
+// loads spread over the step: 4 A + 4 B stages (128 KiB), 5 A + 5 B (160 KiB)
+using T128S4 = TileCfg<128, 128, kLdsXor, 1, 2, 2, 4, 1>;
+using T128S5 = TileCfg<128, 128, kLdsXor, 1, 2, 2, 5, 1>;
 using T256Plain = TileCfg<256, 256, kLdsPlain>;
 using T256Direct = TileCfg<256, 256, kLdsXor, 0>;
 using R256 = RsCfg<256, 256, 2, 2, kLdsXor>;
@@ -204,6 +207,12 @@ const KernelEntry kTable[] = {
     // the 128 x 128 tile on eight waves in two groups that split K (TN)
     ppk_entry<kF16>("tn_f16_128x128x64_ppk", 4),
     ppk_entry<kBF16>("tn_bf16_128x128x64_ppk", 4),
+    // the 128 x 128 tile with its loads spread evenly over the step's MFMAs
+    // before the barrier (A and B rings of equal depth): measured level with
+    // the deeper-ring kernel, an ablation
+    dp_entry<T128S4, kTN, kF16>("tn_f16_128x128x64_s4", 4, false),
+    dp_entry<T128S4, kNN, kBF16>("nn_bf16_128x128x64_s4", 4, false),
+    dp_entry<T128S5, kTN, kF16>("tn_f16_128x128x64_s5", 4, false),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
