@@ -122,6 +122,7 @@ using T128R3 = TileCfg<128, 128, kLdsXor, 1, 2, 2, 3>;  // 4 A + 3 B stages, 112
 // loads spread over the step: 4 A + 4 B stages (128 KiB), 5 A + 5 B (160 KiB)
 using T128S4 = TileCfg<128, 128, kLdsXor, 1, 2, 2, 4, 1>;
 using T128S5 = TileCfg<128, 128, kLdsXor, 1, 2, 2, 5, 1>;
+using T256x128 = TileCfg<256, 128>;  // 3 A + 2 B stages, 128 KiB
 using T256Plain = TileCfg<256, 256, kLdsPlain>;
 using T256Direct = TileCfg<256, 256, kLdsXor, 0>;
 using R256 = RsCfg<256, 256, 2, 2, kLdsXor>;
@@ -213,6 +214,15 @@ const KernelEntry kTable[] = {
     dp_entry<T128S4, kTN, kF16>("tn_f16_128x128x64_s4", 4, false),
     dp_entry<T128S4, kNN, kBF16>("nn_bf16_128x128x64_s4", 4, false),
     dp_entry<T128S5, kTN, kF16>("tn_f16_128x128x64_s5", 4, false),
+    // 256 x 128 tiles: one round where 128 x 128 tiles would need two
+    dp_entry<T256x128, kTN, kF16>("tn_f16_256x128x64", 4, true),
+    dp_entry<T256x128, kTN, kBF16>("tn_bf16_256x128x64", 4, true),
+    dp_entry<T256x128, kNN, kF16>("nn_f16_256x128x64", 4, true),
+    dp_entry<T256x128, kNN, kBF16>("nn_bf16_256x128x64", 4, true),
+    dp_entry<T256x128, kAtTN, kF16>("at_tn_f16_256x128x64", 4, true),
+    dp_entry<T256x128, kAtTN, kBF16>("at_tn_bf16_256x128x64", 4, true),
+    dp_entry<T256x128, kAtNN, kF16>("at_nn_f16_256x128x64", 4, true),
+    dp_entry<T256x128, kAtNN, kBF16>("at_nn_bf16_256x128x64", 4, true),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -226,20 +236,20 @@ constexpr int64_t kMaxLdK = int64_t(1) << 22;
 constexpr int64_t kMaxLdMN = int64_t(1) << 23;
 constexpr int64_t kMaxLdC = (int64_t(1) << 31) - 8;
 
-int find_kernel(int layout, int dtype, int bm, int nsb = 2) {
+int find_kernel(int layout, int dtype, int bm, int bn, int nsb = 2) {
   for (int i = 0; i < kTableSize; ++i)
     if (kTable[i].production && kTable[i].layout == layout && kTable[i].dtype == dtype &&
-        kTable[i].bm == bm && kTable[i].nsb == nsb)
+        kTable[i].bm == bm && kTable[i].bn == bn && kTable[i].nsb == nsb)
       return i;
   return -1;
 }
 
 // Cost model of the automatic choice, in units of one K step of a 256 x 256
-// tile on every CU at once (about 1.3 us on MI355X).  A launch of square tiles
-// of size t runs ceil(tiles / 256 CUs) rounds of one workgroup per CU, each
-// tile taking (KT + kTileFixed) * (t/256)^2 / rate_t units, rate_t the per-CU
-// throughput of that tile size relative to the 256 kernel.  The constants were
-// chosen on measured times of every tile size and split over square, skinny
+// tile on every CU at once (about 1.3 us on MI355X).  A launch of BM x BN
+// tiles runs ceil(tiles / 256 CUs) rounds of one workgroup per CU, each tile
+// taking (KT + kTileFixed) * (BM*BN / 256^2) / rate units, rate the per-CU
+// throughput of that tile relative to the 256 x 256 kernel.  The constants
+// were chosen on measured times of every tile and split over square, skinny
 // and long-K shapes.  The 128 x 128 and 64 x 64 kernels have two rates each:
 // one workgroup per CU (a single round; where the deeper-ring 128 variant
 // runs), and several sharing a CU when there are more tiles than CUs (two of
@@ -247,41 +257,56 @@ int find_kernel(int layout, int dtype, int bm, int nsb = 2) {
 // and NN bf16 shapes put the shared rates at 0.58-0.70 and 0.25-0.45: with
 // the single-round rates there, the choice took the 128 tile where the 256
 // tile was 14-24 % faster (3072^3, 6000 x 6000 x 3000) and the 64 tile where
-// the 128 tile was 30 % faster (2304^3).
+// the 128 tile was 30 % faster (2304^3).  The 256 x 128 tile (128 KiB of LDS,
+// one workgroup per CU) covers in one round what takes the 128 tile two:
+// 6-15 % faster than the square tiles on 2304^3-2816^3, 4608^3 and
+// 1024 x 8192 x 8192 (both orientations, TN and NN).  On the same sweeps its
+// rate 0.76 brings the choice from 1.9 % to 0.4 % behind the fastest kernel
+// on average (any rate in 0.66-0.82 gives the same choices but one).
 constexpr int64_t kCUs = 256;
-const int kSizes[3] = {256, 128, 64};
-const double kRate[3] = {1.0, 0.8, 0.5};  // sustained rate relative to the 256 x 256 tile
-const double kRateShared[3] = {1.0, 0.64, 0.37};  // ... with more tiles than CUs
+struct TileCand {
+  int bm, bn;
+  double rate;         // sustained rate relative to the 256 x 256 tile
+  double rate_shared;  // ... with more tiles than CUs
+};
+// in order of preference on equal estimates
+const TileCand kCand[4] = {
+    {256, 256, 1.0, 1.0}, {256, 128, 0.76, 0.76}, {128, 128, 0.8, 0.64}, {64, 64, 0.5, 0.37}};
+constexpr int kNumCand = 4;
 constexpr double kTileFixed = 3.0;        // prologue and epilogue of a tile, in K steps
 constexpr double kSplitFixed = 6.9;       // the fixup launch and the wait for it
 constexpr double kSlotCost = 0.055;       // one 256 KiB partial sum written and read back
 constexpr int kMaxAutoSplit = 64;
 constexpr int64_t kMaxSlots = 1024;       // 256 MiB of partial sums at most
 
-double dp_cost(int i, int64_t M, int64_t N, int64_t KT) {
-  const int64_t t = kSizes[i];
-  const int64_t tiles = ((M + t - 1) / t) * ((N + t - 1) / t);
-  const double rate = tiles > kCUs ? kRateShared[i] : kRate[i];
-  return (double)((tiles + kCUs - 1) / kCUs) * ((double)KT + kTileFixed) * (double)(t * t) /
-         65536.0 / rate;
+int64_t tile_count(const TileCand &c, int64_t M, int64_t N) {
+  return ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
 }
 
-// Automatic choice without a K split: the tile size with the least estimated
-// time; ties go to the larger tile.  A single round of 128 x 128 tiles over at
-// least kDeepRingSteps K steps takes the ring with one more stage per operand:
-// one workgroup per CU either way, and the deeper prefetch hides the load
-// latency (measured 3-17 % faster there).  With more than one round two
+double dp_cost(int i, int64_t M, int64_t N, int64_t KT) {
+  const TileCand &c = kCand[i];
+  const int64_t tiles = tile_count(c, M, N);
+  const double rate = tiles > kCUs ? c.rate_shared : c.rate;
+  return (double)((tiles + kCUs - 1) / kCUs) * ((double)KT + kTileFixed) *
+         (double)(c.bm * c.bn) / 65536.0 / rate;
+}
+
+// Automatic choice without a K split: the tile with the least estimated
+// time; ties go to the earlier candidate.  A single round of 128 x 128 tiles
+// over at least kDeepRingSteps K steps takes the ring with one more stage per
+// operand: one workgroup per CU either way, and the deeper prefetch hides the
+// load latency (measured 3-17 % faster there).  With more than one round two
 // workgroups share a CU, which the deeper ring's LDS would forbid.
 constexpr int64_t kDeepRingSteps = 24;
 int auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K) {
   const int64_t KT = K > 0 ? (K + 63) / 64 : 1;
   int best = 0;
-  for (int i = 1; i < 3; ++i)
+  for (int i = 1; i < kNumCand; ++i)
     if (dp_cost(i, M, N, KT) < dp_cost(best, M, N, KT)) best = i;
-  const int64_t t = kSizes[best];
-  if (t == 128 && ((M + t - 1) / t) * ((N + t - 1) / t) <= kCUs && KT >= kDeepRingSteps)
-    return find_kernel(layout, dtype, 128, 3);
-  return find_kernel(layout, dtype, kSizes[best]);
+  const TileCand &c = kCand[best];
+  if (c.bm == 128 && c.bn == 128 && tile_count(c, M, N) <= kCUs && KT >= kDeepRingSteps)
+    return find_kernel(layout, dtype, 128, 128, 3);
+  return find_kernel(layout, dtype, c.bm, c.bn);
 }
 
 // K split of the last, partial round of 256 x 256 tiles (the tail): the
@@ -322,7 +347,7 @@ Plan split_plan(int layout, int dtype, int64_t M, int64_t N, int64_t K, int spli
     }
   }
   if (S < 2 || S > KT || tail * S > (int64_t(1) << 20)) return p;
-  p.kidx = find_kernel(layout, dtype, 256);
+  p.kidx = find_kernel(layout, dtype, 256, 256);
   p.split = (int)S;
   p.sk_tiles = tail;
   p.dp_tiles = tiles - tail;
@@ -342,7 +367,7 @@ Plan choose(int layout, int dtype, int64_t M, int64_t N, int64_t K, int split, s
   if (split > 0) return sk;
   const int64_t KT = (K + 63) / 64;
   double best = dp_cost(0, M, N, KT);
-  for (int i = 1; i < 3; ++i) best = std::min(best, dp_cost(i, M, N, KT));
+  for (int i = 1; i < kNumCand; ++i) best = std::min(best, dp_cost(i, M, N, KT));
   return sk.cost < best ? sk : dp;
 }
 
