@@ -450,7 +450,7 @@ SWEEP_CHECK = ([("tn", "f16", s, s, s) for s in (2304, 2816, 3328, 3840, 4608)]
                   ("tn", "f16", 2560, 8192, 4096)]
                + [("nn", "bf16", s, s, s) for s in (2048, 2560, 3072, 4096, 6144)]
                + [("nn", "bf16", 1024, 8192, 8192), ("nn", "bf16", 6000, 6000, 3000)])
-SWEEP_TILES = ("256x256x64", "256x128x64", "128x128x64_r3", "128x128x64", "64x64x64")
+SWEEP_TILES = ("256x256x64", "192x256x64", "256x128x64", "128x128x64_r3", "128x128x64", "64x64x64")
 
 
 def sweep(which: str = "tn") -> int:

@@ -123,6 +123,7 @@ using T128R3 = TileCfg<128, 128, kLdsXor, 1, 2, 2, 3>;  // 4 A + 3 B stages, 112
 using T128S4 = TileCfg<128, 128, kLdsXor, 1, 2, 2, 4, 1>;
 using T128S5 = TileCfg<128, 128, kLdsXor, 1, 2, 2, 5, 1>;
 using T256x128 = TileCfg<256, 128>;  // 3 A + 2 B stages, 128 KiB
+using T192x256 = TileCfg<192, 256>;  // 3 A + 2 B stages, 136 KiB
 using T256Plain = TileCfg<256, 256, kLdsPlain>;
 using T256Direct = TileCfg<256, 256, kLdsXor, 0>;
 using R256 = RsCfg<256, 256, 2, 2, kLdsXor>;
@@ -223,6 +224,12 @@ const KernelEntry kTable[] = {
     dp_entry<T256x128, kAtTN, kBF16>("at_tn_bf16_256x128x64", 4, true),
     dp_entry<T256x128, kAtNN, kF16>("at_nn_f16_256x128x64", 4, true),
     dp_entry<T256x128, kAtNN, kBF16>("at_nn_bf16_256x128x64", 4, true),
+    // 192 x 256 tiles (A k-contiguous only: 192-row A tiles; the 384-byte
+    // rows of an m-contiguous A tile do not fill whole 1 KiB load segments)
+    dp_entry<T192x256, kTN, kF16>("tn_f16_192x256x64", 4, true),
+    dp_entry<T192x256, kTN, kBF16>("tn_bf16_192x256x64", 4, true),
+    dp_entry<T192x256, kNN, kF16>("nn_f16_192x256x64", 4, true),
+    dp_entry<T192x256, kNN, kBF16>("nn_bf16_192x256x64", 4, true),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -262,7 +269,14 @@ int find_kernel(int layout, int dtype, int bm, int bn, int nsb = 2) {
 // 6-15 % faster than the square tiles on 2304^3-2816^3, 4608^3 and
 // 1024 x 8192 x 8192 (both orientations, TN and NN).  On the same sweeps its
 // rate 0.76 brings the choice from 1.9 % to 0.4 % behind the fastest kernel
-// on average (any rate in 0.66-0.82 gives the same choices but one).
+// on average (any rate in 0.66-0.82 gives the same choices but one).  The
+// 192 x 256 tile (136 KiB, one workgroup per CU) fills the CUs where 256 x 256
+// tiles leave a partial round (3072^3: 192 tiles against 144; 6144^3: three
+// whole rounds against two and a quarter): the fastest kernel on 12 of the 49
+// sweep shapes, 3-18 % ahead of every other tile, and slower where 256 x 256
+// tiles fill whole rounds (8192^3).  With it at rate 0.83 (any rate in
+// 0.78-0.92 gives the same choices) the choice is 0.3 % behind the fastest
+// kernel on average, 47 of 49 shapes within 2 %, against 2.4 % without it.
 constexpr int64_t kCUs = 256;
 struct TileCand {
   int bm, bn;
@@ -270,9 +284,12 @@ struct TileCand {
   double rate_shared;  // ... with more tiles than CUs
 };
 // in order of preference on equal estimates
-const TileCand kCand[4] = {
-    {256, 256, 1.0, 1.0}, {256, 128, 0.76, 0.76}, {128, 128, 0.8, 0.64}, {64, 64, 0.5, 0.37}};
-constexpr int kNumCand = 4;
+const TileCand kCand[5] = {{256, 256, 1.0, 1.0},
+                           {192, 256, 0.83, 0.83},
+                           {256, 128, 0.76, 0.76},
+                           {128, 128, 0.8, 0.64},
+                           {64, 64, 0.5, 0.37}};
+constexpr int kNumCand = 5;
 constexpr double kTileFixed = 3.0;        // prologue and epilogue of a tile, in K steps
 constexpr double kSplitFixed = 6.9;       // the fixup launch and the wait for it
 constexpr double kSlotCost = 0.055;       // one 256 KiB partial sum written and read back
@@ -298,11 +315,15 @@ double dp_cost(int i, int64_t M, int64_t N, int64_t KT) {
 // load latency (measured 3-17 % faster there).  With more than one round two
 // workgroups share a CU, which the deeper ring's LDS would forbid.
 constexpr int64_t kDeepRingSteps = 24;
+// Candidates without a kernel for the layout and dtype are skipped.
+bool has_cand(int i, int layout, int dtype) {
+  return find_kernel(layout, dtype, kCand[i].bm, kCand[i].bn) >= 0;
+}
 int auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K) {
   const int64_t KT = K > 0 ? (K + 63) / 64 : 1;
   int best = 0;
   for (int i = 1; i < kNumCand; ++i)
-    if (dp_cost(i, M, N, KT) < dp_cost(best, M, N, KT)) best = i;
+    if (has_cand(i, layout, dtype) && dp_cost(i, M, N, KT) < dp_cost(best, M, N, KT)) best = i;
   const TileCand &c = kCand[best];
   if (c.bm == 128 && c.bn == 128 && tile_count(c, M, N) <= kCUs && KT >= kDeepRingSteps)
     return find_kernel(layout, dtype, 128, 128, 3);
@@ -367,7 +388,8 @@ Plan choose(int layout, int dtype, int64_t M, int64_t N, int64_t K, int split, s
   if (split > 0) return sk;
   const int64_t KT = (K + 63) / 64;
   double best = dp_cost(0, M, N, KT);
-  for (int i = 1; i < kNumCand; ++i) best = std::min(best, dp_cost(i, M, N, KT));
+  for (int i = 1; i < kNumCand; ++i)
+    if (has_cand(i, layout, dtype)) best = std::min(best, dp_cost(i, M, N, KT));
   return sk.cost < best ? sk : dp;
 }
 

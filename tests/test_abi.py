@@ -202,11 +202,8 @@ def test_kernel_table_and_auto_choice():
     assert tab[hgemm.auto_kernel(3, 1, 1536, 1536, 1536)]["name"] == "at_nn_bf16_128x128x64_r3"
     assert tab[hgemm.auto_kernel(1, 1, 2048, 2048, 1472)]["name"] == "nn_bf16_128x128x64"
     # tiles that share CUs (more tiles than CUs) run at the measured shared
-    # rates: 3072^3 and 6000 x 6000 x 3000 take the 256 x 256 tile (14 % and 24 %
-    # faster there than 128 x 128), 1024^3 still 64 x 64, 2048 x 2048 x 8192
-    # one round of the deeper-ring 128 x 128 kernel (28 % faster than 256 x 128)
-    assert tab[hgemm.auto_kernel(0, 0, 3072, 3072, 3072)]["bm"] == 256
-    assert tab[hgemm.auto_kernel(0, 0, 6000, 6000, 3000)]["bm"] == 256
+    # rates: 1024^3 stays 64 x 64; 2048 x 2048 x 8192 takes one round of the
+    # deeper-ring 128 x 128 kernel (28 % faster than 256 x 128)
     assert tab[hgemm.auto_kernel(0, 0, 1024, 1024, 1024)]["bm"] == 64
     assert tab[hgemm.auto_kernel(0, 0, 2048, 2048, 8192)]["name"] == "tn_f16_128x128x64_r3"
     # one round of 256 x 128 tiles where 128 x 128 tiles would take two: the
@@ -214,10 +211,18 @@ def test_kernel_table_and_auto_choice():
     assert tab[hgemm.auto_kernel(0, 0, 1024, 8192, 8192)]["name"] == "tn_f16_256x128x64"
     assert tab[hgemm.auto_kernel(0, 0, 8192, 1024, 8192)]["name"] == "tn_f16_256x128x64"
     assert tab[hgemm.auto_kernel(1, 1, 1024, 8192, 8192)]["name"] == "nn_bf16_256x128x64"
-    for s in (2304, 2560, 2816, 4608):
+    for s in (2304, 2560, 2816):
         assert tab[hgemm.auto_kernel(0, 0, s, s, s)]["name"] == "tn_f16_256x128x64", s
-    # and not where the square tiles were faster on the same sweeps
-    for s in (4096, 6144, 8192):
+    # 192 x 256 tiles where they fill the CUs better than 256 x 256 ones (3-18 %
+    # ahead of every other tile on the sweeps): TN and NN only, A k-contiguous;
+    # with A stored transposed the 256 x 256 tile stays
+    for M, N, K in ((3072, 3072, 3072), (6144, 6144, 6144), (4608, 4608, 4608),
+                    (6000, 6000, 3000), (7000, 5000, 4000)):
+        assert tab[hgemm.auto_kernel(0, 0, M, N, K)]["name"] == "tn_f16_192x256x64", (M, N, K)
+    assert tab[hgemm.auto_kernel(1, 1, 3072, 3072, 3072)]["name"] == "nn_bf16_192x256x64"
+    assert tab[hgemm.auto_kernel(2, 0, 3072, 3072, 3072)]["name"] == "at_tn_f16_256x256x64"
+    # and not where the 256 x 256 tile was faster on the same sweeps
+    for s in (4096, 5120, 8192):
         assert tab[hgemm.auto_kernel(0, 0, s, s, s)]["name"] == "tn_f16_256x256x64", s
     assert tab[hgemm.auto_kernel(0, 0, 256, 16384, 4096)]["name"] == "tn_f16_128x128x64_r3"
 
