@@ -450,6 +450,25 @@ SWEEP_CHECK = ([("tn", "f16", s, s, s) for s in (2304, 2816, 3328, 3840, 4608)]
                   ("tn", "f16", 2560, 8192, 4096)]
                + [("nn", "bf16", s, s, s) for s in (2048, 2560, 3072, 4096, 6144)]
                + [("nn", "bf16", 1024, 8192, 8192), ("nn", "bf16", 6000, 6000, 3000)])
+
+
+def sweep_wide(count: int = 60, seed: int = 20261203):
+    """A third set, drawn at random and not used to set any constant: TN f16
+    and NN bf16 (two to one), M and N multiples of 64 in [512, 12288], K a
+    multiple of 64 in [256, 16384], at most 2 TFLOP a shape."""
+    import numpy as np
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    while len(out) < count:
+        M, N = (64 * int(x) for x in g.integers(8, 193, size=2))
+        K = 64 * int(g.integers(4, 257))
+        if 2.0 * M * N * K > 2.0e12:
+            continue
+        lay, dt = ("tn", "f16") if len(out) % 3 != 2 else ("nn", "bf16")
+        out.append((lay, dt, M, N, K))
+    return out
+
+
 SWEEP_TILES = ("256x256x64", "192x256x64", "256x128x64", "128x128x64_r3", "128x128x64", "64x64x64")
 
 
@@ -462,7 +481,7 @@ def sweep(which: str = "tn") -> int:
     workspace, hgemm_gemm_ws runs the K split of the tail where its cost
     model expects a gain), the automatic choice without a workspace, and how
     far it, and the call with a workspace, fall behind the best candidate; a
-    summary line at the end.  `which`: "tn" (SWEEP_SHAPES) or "check"
+    summary line at the end.  `which`: "tn" (SWEEP_SHAPES), "wide" (sweep_wide()) or "check"
     (SWEEP_CHECK)."""
     import numpy as np
     import torch
@@ -471,7 +490,7 @@ def sweep(which: str = "tn") -> int:
     hold = QueueHold()
     regrets, regrets_ws = [], []
     shapes = ([("tn", "f16", M, N, K) for M, N, K in SWEEP_SHAPES] if which == "tn"
-              else SWEEP_CHECK)
+              else SWEEP_CHECK if which == "check" else sweep_wide())
     for lay, dt, M, N, K in shapes:
         g = torch.Generator(device="cuda").manual_seed(M * 131 + N * 17 + K)
         tdt = torch.float16 if dt == "f16" else torch.bfloat16
@@ -927,9 +946,10 @@ def main() -> int:
     ap.add_argument("--clock-trace", type=int, default=0, metavar="LAUNCHES",
                     help="print the engine clock over this many back-to-back launches of the "
                          "workload's kernel after 2 s idle, and exit")
-    ap.add_argument("--sweep", choices=("tn", "check"), default=None,
+    ap.add_argument("--sweep", choices=("tn", "check", "wide"), default=None,
                     help="the automatic choice against every production kernel over a grid of "
-                         "TN f16 shapes ('tn') or a second set with NN bf16 ('check'), and exit")
+                         "TN f16 shapes ('tn'), a second set with NN bf16 ('check') or a seeded "
+                         "random third set ('wide'), and exit")
     ap.add_argument("--phases", type=int, default=0, metavar="LAUNCHES",
                     help="after the settle phase, time the main loop's phases (wait, barrier, "
                          "rest) with the workload kernel's '_ph' copy over this many launches, "

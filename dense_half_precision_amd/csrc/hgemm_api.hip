@@ -294,6 +294,14 @@ constexpr double kTileFixed = 3.0;        // prologue and epilogue of a tile, in
 constexpr double kSplitFixed = 6.9;       // the fixup launch and the wait for it
 constexpr double kSlotCost = 0.055;       // one 256 KiB partial sum written and read back
 constexpr int kMaxAutoSplit = 64;
+// The split runs only where its estimate is below kSplitMargin times the best
+// unsplit one.  On the 32 shapes of three sweeps (49 tuning and check shapes,
+// 60 drawn at random) where a workspace allows it, every split estimated
+// below 0.86 of the unsplit tiles measured faster (3-36 %; 6x for
+// 512 x 512 x 65536), while those estimated at 0.86-0.97 ranged from 13 %
+// slower to 8 % faster, half of them slower: the estimate leaves out costs
+// that the 192 x 256 and 256 x 128 tiles do not have.
+constexpr double kSplitMargin = 0.86;
 constexpr int64_t kMaxSlots = 1024;       // 256 MiB of partial sums at most
 
 int64_t tile_count(const TileCand &c, int64_t M, int64_t N) {
@@ -390,7 +398,7 @@ Plan choose(int layout, int dtype, int64_t M, int64_t N, int64_t K, int split, s
   double best = dp_cost(0, M, N, KT);
   for (int i = 1; i < kNumCand; ++i)
     if (has_cand(i, layout, dtype)) best = std::min(best, dp_cost(i, M, N, KT));
-  return sk.cost < best ? sk : dp;
+  return sk.cost < kSplitMargin * best ? sk : dp;
 }
 
 struct Call {

@@ -107,11 +107,15 @@ def test_split_workspace_size_and_validation():
     forced split, all decided on the host before any launch."""
     inv, uns = hgemm.ERR_INVALID_ARG, hgemm.ERR_UNSUPPORTED
     size = hgemm.gemm_ws_size
-    # 6144^2: 24 x 24 = 576 tiles of 256 x 256 = 2 rounds of 256 CUs + a tail
-    # of 64 tiles; the estimate is least at 4 segments (one wave of 256), 256
-    # KiB of partial sums each
-    assert size(0, 1, 6144, 6144, 6144, "f16") == 64 * 4 * 256 * 256 * 4
-    assert size(0, 0, 6144, 6144, 6144, "bf16") == 64 * 4 * 256 * 256 * 4
+    # 7168^3: 28 x 28 = 784 tiles of 256 x 256 = 3 rounds of 256 CUs + a tail
+    # of 16 tiles of 112 K steps; the estimate is least at 14 segments (224
+    # of them, one wave), 256 KiB of partial sums each
+    assert size(0, 1, 7168, 7168, 7168, "f16") == 16 * 14 * 256 * 256 * 4
+    assert size(0, 0, 7168, 7168, 7168, "bf16") == 16 * 14 * 256 * 256 * 4
+    # 6144^3: 576 tiles = 2 rounds + a tail of 64, but 192 x 256 tiles fill
+    # three whole rounds and run unsplit as fast as the best split: no split,
+    # no workspace
+    assert size(0, 1, 6144, 6144, 6144, "f16") == 0
     assert size(0, 1, 8192, 8192, 8192, "f16") == 0      # 1024 tiles: whole rounds
     assert size(0, 1, 2048, 2048, 64, "f16") == 0        # one K step: nothing to split
     # 512 x 512 x 65536: 4 tiles, 1024 K steps: 64 segments each fill the CUs
@@ -125,7 +129,7 @@ def test_split_workspace_size_and_validation():
 
     g = hgemm.hgemm_gemm_ws
     M = N = K = 6144
-    need = size(0, 1, M, N, K, "f16")
+    need = 64 * 4 * 256 * 256 * 4  # a forced split in 4: the 64 tail tiles' partial sums
 
     def call(split, ws=FAKE, nbytes=need, kernel=None, m=M, n=N, k=K):
         return g(0, 1, m, n, k, "f16", 1.0, FAKE, k, FAKE, k, 0.0, FAKE, n, ws, nbytes,
@@ -159,13 +163,13 @@ def test_noalloc_refusals_on_the_host():
         return f(opA, opB, m, n, k, dt, 1.0, ptr, lda, ptr, ldb, 0.0, ptr,
                  ldc if ldc is not None else n, 0)
     assert hgemm.lib().hgemm_status_string(hgemm.ERR_SCRATCH).decode().startswith("the K split")
-    # over the limit: 7680^2 x 7680 has a tail of 132 tiles; 4608^2 x 8192 68
-    over = [(m, n, k) for (m, n, k) in ((7680, 7680, 7680), (4608, 4608, 8192), (3328, 3328, 16384))
+    # over the limit: 2560^2 x 16384 is 100 tiles of 256 K steps, split in 5
+    over = [(m, n, k) for (m, n, k) in ((2560, 2560, 16384), (2048, 3072, 16384))
             if size(0, 1, m, n, k, "f16") > lim]
     assert over, "no shape over the scratch limit among the candidates"
     for m, n, k in over:
         assert call(m, n, k) == hgemm.ERR_SCRATCH
-    assert size(0, 1, 6144, 6144, 6144, "f16") == lim  # exactly the limit: accepted (GPU test)
+    assert size(0, 1, 4096, 4608, 6144, "f16") == lim  # exactly the limit: accepted (GPU test)
     assert call(-1, 8, 8) == hgemm.ERR_INVALID_ARG
     assert call(8, 8, 8, opA=2) == hgemm.ERR_INVALID_ARG
     assert call(8, 8, 8, dt=7) == hgemm.ERR_INVALID_ARG

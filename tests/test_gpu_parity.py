@@ -124,6 +124,36 @@ def test_persistent_many_tiles(name):
     assert np.array_equal(C, plain), f"{name}: differs from the plain launch"
 
 
+@pytest.mark.parametrize("name", ["tn_f16_192x256x64", "nn_bf16_192x256x64", "tn_f16_256x128x64",
+                                  "nn_bf16_256x128x64", "at_tn_bf16_256x128x64",
+                                  "at_nn_f16_256x128x64"])
+def test_rectangular_tiles_at_scale(name):
+    """The 192 x 256 and 256 x 128 production kernels on a few rounds of
+    tiles with ragged last tile rows and columns (3000 = 15 x 192 + 120 =
+    11 x 256 + 184) and a K tail: whole output by projection, a stratified
+    sample element by element, and the same bits as the 256 x 256 kernel,
+    which sums every element over the same K slices in the same order."""
+    k = hgemm.kernel_table()[hgemm.kernel_index(name)]
+    layout = ("tn", "nn", "at_tn", "at_nn")[k["layout"]]
+    dtype = "f16" if k["dtype"] == hgemm.F16 else "bf16"
+    M, N, K = 3000, 3080, 3112
+    print(f"\n[parity] {name} {M}x{N}x{K}", flush=True)
+    opA, opB = int(layout.startswith("at_")), int(layout.endswith("tn"))
+    A = inputs.draw((M, K), dtype, "uniform", 91)
+    Bl = inputs.draw((K, N), dtype, "uniform", 92)
+    As = helpers.stored(A, opA == 1, 0, 0)
+    Bs = helpers.stored(Bl, opB == 1, 0, 0)
+    Cin = np.zeros((M, N), dtype=np.uint16)
+    C = helpers.gpu_gemm_general(opA, opB, dtype, M, N, K, As, Bs, 1.0, 0.0, Cin, k["index"])
+    square = hgemm.kernel_index(name.replace(name[-10:], "256x256x64"))
+    C256 = helpers.gpu_gemm_general(opA, opB, dtype, M, N, K, As, Bs, 1.0, 0.0, Cin, square)
+    assert np.array_equal(C, C256), f"{name}: differs from the 256 x 256 kernel"
+    r, c = inputs.stratified_samples(M, N, 93)
+    ref = oracle.gemm_sampled(opA, opB, dtype, M, N, K, As, Bs, r, c)
+    helpers.parity(C[r, c], ref, dtype, name)
+    helpers.freivalds(C, A, np.ascontiguousarray(Bl.T), "tn", dtype)
+
+
 @pytest.mark.parametrize("name", ["tn_f16_256x256x64_pp", "tn_bf16_256x256x64_pp"])
 def test_ping_pong_matches_production_bits(name):
     """The two-group kernel sums the same 32-k slices in the same order as the

@@ -12,10 +12,10 @@ from dense_half_precision_amd import hgemm, inputs
 pytestmark = pytest.mark.gpu
 
 # (opA, opB, dtype, M, N, K, alpha, beta, pad): the first needs the whole
-# scratch (64 MiB of partial sums), the second less, with alpha/beta and
-# padded leading dimensions
+# scratch (64 MiB of partial sums: a tail of 32 tiles in 8 segments), the
+# second less, with alpha/beta and padded leading dimensions
 CALLS = [
-    (hgemm.OP_N, hgemm.OP_T, "f16", 6144, 6144, 6144, 1.0, 0.0, 0),
+    (hgemm.OP_N, hgemm.OP_T, "f16", 4096, 4608, 6144, 1.0, 0.0, 0),
     (hgemm.OP_N, hgemm.OP_N, "bf16", 4352, 4352, 4096, 0.75, -0.5, 8),
 ]
 
