@@ -469,7 +469,12 @@ def sweep_wide(count: int = 60, seed: int = 20261203):
     return out
 
 
-SWEEP_TILES = ("256x256x64", "192x256x64", "256x128x64", "128x128x64_r3", "128x128x64", "64x64x64")
+# A fourth set: single rounds of 64 x 64 tiles (512^2 to 1024^2), K from 1024 to 16384,
+# where the operands fall out of the L2 at some K and the ring depth decides.
+SWEEP_SMALL = [("tn", "f16", m, m, k) for m in (512, 640, 768, 1024)
+               for k in (1024, 2048, 3072, 4096, 8192, 16384)]
+SWEEP_TILES = ("256x256x64", "192x256x64", "256x128x64", "128x128x64_r3", "128x128x64", "64x64x64_r4",
+               "64x64x64")
 
 
 def sweep(which: str = "tn") -> int:
@@ -481,8 +486,8 @@ def sweep(which: str = "tn") -> int:
     workspace, hgemm_gemm_ws runs the K split of the tail where its cost
     model expects a gain), the automatic choice without a workspace, and how
     far it, and the call with a workspace, fall behind the best candidate; a
-    summary line at the end.  `which`: "tn" (SWEEP_SHAPES), "wide" (sweep_wide()) or "check"
-    (SWEEP_CHECK)."""
+    summary line at the end.  `which`: "tn" (SWEEP_SHAPES), "check" (SWEEP_CHECK), "wide"
+    (sweep_wide()) or "small" (SWEEP_SMALL)."""
     import numpy as np
     import torch
     from dense_half_precision_amd import hgemm
@@ -490,7 +495,8 @@ def sweep(which: str = "tn") -> int:
     hold = QueueHold()
     regrets, regrets_ws = [], []
     shapes = ([("tn", "f16", M, N, K) for M, N, K in SWEEP_SHAPES] if which == "tn"
-              else SWEEP_CHECK if which == "check" else sweep_wide())
+              else SWEEP_CHECK if which == "check" else SWEEP_SMALL if which == "small"
+              else sweep_wide())
     for lay, dt, M, N, K in shapes:
         g = torch.Generator(device="cuda").manual_seed(M * 131 + N * 17 + K)
         tdt = torch.float16 if dt == "f16" else torch.bfloat16
@@ -946,10 +952,11 @@ def main() -> int:
     ap.add_argument("--clock-trace", type=int, default=0, metavar="LAUNCHES",
                     help="print the engine clock over this many back-to-back launches of the "
                          "workload's kernel after 2 s idle, and exit")
-    ap.add_argument("--sweep", choices=("tn", "check", "wide"), default=None,
+    ap.add_argument("--sweep", choices=("tn", "check", "wide", "small"), default=None,
                     help="the automatic choice against every production kernel over a grid of "
-                         "TN f16 shapes ('tn'), a second set with NN bf16 ('check') or a seeded "
-                         "random third set ('wide'), and exit")
+                         "TN f16 shapes ('tn'), a second set with NN bf16 ('check'), a seeded "
+                         "random third set ('wide') or single rounds of 64 x 64 tiles ('small'), "
+                         "and exit")
     ap.add_argument("--phases", type=int, default=0, metavar="LAUNCHES",
                     help="after the settle phase, time the main loop's phases (wait, barrier, "
                          "rest) with the workload kernel's '_ph' copy over this many launches, "

@@ -124,6 +124,7 @@ using T128S4 = TileCfg<128, 128, kLdsXor, 1, 2, 2, 4, 1>;
 using T128S5 = TileCfg<128, 128, kLdsXor, 1, 2, 2, 5, 1>;
 using T256x128 = TileCfg<256, 128>;  // 3 A + 2 B stages, 128 KiB
 using T192x256 = TileCfg<192, 256>;  // 3 A + 2 B stages, 136 KiB
+using T64R4 = TileCfg<64, 64, kLdsXor, 1, 2, 2, 4>;  // 5 A + 4 B stages, 72 KiB
 using T256Plain = TileCfg<256, 256, kLdsPlain>;
 using T256Direct = TileCfg<256, 256, kLdsXor, 0>;
 using R256 = RsCfg<256, 256, 2, 2, kLdsXor>;
@@ -230,6 +231,16 @@ const KernelEntry kTable[] = {
     dp_entry<T192x256, kTN, kBF16>("tn_bf16_192x256x64", 4, true),
     dp_entry<T192x256, kNN, kF16>("nn_f16_192x256x64", 4, true),
     dp_entry<T192x256, kNN, kBF16>("nn_bf16_192x256x64", 4, true),
+    // the 64 x 64 tile with a deeper LDS ring, for a single round of tiles
+    // whose operands do not stay in the L2
+    dp_entry<T64R4, kTN, kF16>("tn_f16_64x64x64_r4", 4, true),
+    dp_entry<T64R4, kTN, kBF16>("tn_bf16_64x64x64_r4", 4, true),
+    dp_entry<T64R4, kNN, kF16>("nn_f16_64x64x64_r4", 4, true),
+    dp_entry<T64R4, kNN, kBF16>("nn_bf16_64x64x64_r4", 4, true),
+    dp_entry<T64R4, kAtTN, kF16>("at_tn_f16_64x64x64_r4", 4, true),
+    dp_entry<T64R4, kAtTN, kBF16>("at_tn_bf16_64x64x64_r4", 4, true),
+    dp_entry<T64R4, kAtNN, kF16>("at_nn_f16_64x64x64_r4", 4, true),
+    dp_entry<T64R4, kAtNN, kBF16>("at_nn_bf16_64x64x64_r4", 4, true),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -323,6 +334,14 @@ double dp_cost(int i, int64_t M, int64_t N, int64_t KT) {
 // load latency (measured 3-17 % faster there).  With more than one round two
 // workgroups share a CU, which the deeper ring's LDS would forbid.
 constexpr int64_t kDeepRingSteps = 24;
+// A single round of 64 x 64 tiles takes the ring with 5 A + 4 B stages once A
+// and B together pass kDeepRing64Bytes: the default ring loads two steps
+// ahead, which at this tile's short steps (8 MFMAs a wave) no longer covers
+// the load latency once the operands stop staying in the L2.  Measured on 24
+// single-round TN shapes (512^2 to 1024^2, K 1024 to 16384): 1.5-1.8x faster
+// on all 16 whose A and B pass 7 MiB, 1-4 % slower on the 8 that stay at or
+// under 8 MiB (two of them, at 8 MiB, on the wrong side of the threshold).
+constexpr int64_t kDeepRing64Bytes = int64_t(6) << 20;
 // Candidates without a kernel for the layout and dtype are skipped.
 bool has_cand(int i, int layout, int dtype) {
   return find_kernel(layout, dtype, kCand[i].bm, kCand[i].bn) >= 0;
@@ -335,6 +354,8 @@ int auto_kernel(int layout, int dtype, int64_t M, int64_t N, int64_t K) {
   const TileCand &c = kCand[best];
   if (c.bm == 128 && c.bn == 128 && tile_count(c, M, N) <= kCUs && KT >= kDeepRingSteps)
     return find_kernel(layout, dtype, 128, 128, 3);
+  if (c.bm == 64 && c.bn == 64 && tile_count(c, M, N) <= kCUs && 2 * (M + N) * K > kDeepRing64Bytes)
+    return find_kernel(layout, dtype, 64, 64, 4);
   return find_kernel(layout, dtype, c.bm, c.bn);
 }
 

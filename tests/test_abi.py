@@ -208,7 +208,16 @@ def test_kernel_table_and_auto_choice():
     # tiles that share CUs (more tiles than CUs) run at the measured shared
     # rates: 1024^3 stays 64 x 64; 2048 x 2048 x 8192 takes one round of the
     # deeper-ring 128 x 128 kernel (28 % faster than 256 x 128)
-    assert tab[hgemm.auto_kernel(0, 0, 1024, 1024, 1024)]["bm"] == 64
+    assert tab[hgemm.auto_kernel(0, 0, 1024, 1024, 1024)]["name"] == "tn_f16_64x64x64"
+    # a single round of 64 x 64 tiles whose A and B pass 6 MiB takes the ring
+    # with 5 A + 4 B stages (1.5-1.8x faster measured there); under it, or with
+    # more tiles than CUs, the default ring
+    assert tab[hgemm.auto_kernel(0, 0, 512, 512, 8192)]["name"] == "tn_f16_64x64x64_r4"
+    assert tab[hgemm.auto_kernel(0, 0, 640, 640, 3072)]["name"] == "tn_f16_64x64x64_r4"
+    assert tab[hgemm.auto_kernel(1, 1, 1024, 1024, 16384)]["name"] == "nn_bf16_64x64x64_r4"
+    assert tab[hgemm.auto_kernel(3, 0, 512, 512, 65536)]["name"] == "at_nn_f16_64x64x64_r4"
+    assert tab[hgemm.auto_kernel(0, 0, 512, 512, 2048)]["name"] == "tn_f16_64x64x64"
+    assert tab[hgemm.auto_kernel(0, 0, 768, 768, 2048)]["name"] == "tn_f16_64x64x64"
     assert tab[hgemm.auto_kernel(0, 0, 2048, 2048, 8192)]["name"] == "tn_f16_128x128x64_r3"
     # one round of 256 x 128 tiles where 128 x 128 tiles would take two: the
     # measured sweeps put it 6-15 % ahead of every square tile on these

@@ -86,11 +86,13 @@ def test_every_kernel_ragged(kernel):
         helpers.parity(C, oracle.hgemm(layout, dtype, A, B), dtype, f"{k['name']} gm={gm} xcd={xcd}")
 
 
-@pytest.mark.parametrize("name", ["tn_f16_128x128x64_r3", "nn_bf16_128x128x64_r3"])
+@pytest.mark.parametrize("name", ["tn_f16_128x128x64_r3", "nn_bf16_128x128x64_r3",
+                                  "tn_bf16_64x64x64_r4", "nn_f16_64x64x64_r4"])
 def test_deep_ring_k_tails(name):
-    """The 128 x 128 kernel with four A and three B LDS stages loads three
-    steps ahead: K of one to six steps puts the partial last step at each of
-    the prologue's loads and at the loop's, with ragged M and N."""
+    """The deeper-ring kernels (128 x 128 with four A and three B LDS stages,
+    64 x 64 with five and four) load three or four steps ahead: K of one to
+    six steps puts the partial last step at each of the prologue's loads and
+    at the loop's, with ragged M and N."""
     k = hgemm.kernel_table()[hgemm.kernel_index(name)]
     layout = "tn" if k["layout"] == hgemm.TN else "nn"
     dtype = "f16" if k["dtype"] == hgemm.F16 else "bf16"
