@@ -473,8 +473,8 @@ def sweep_wide(count: int = 60, seed: int = 20261203):
 # where the operands fall out of the L2 at some K and the ring depth decides.
 SWEEP_SMALL = [("tn", "f16", m, m, k) for m in (512, 640, 768, 1024)
                for k in (1024, 2048, 3072, 4096, 8192, 16384)]
-SWEEP_TILES = ("256x256x64", "192x256x64", "256x128x64", "128x128x64_r3", "128x128x64", "64x64x64_r4",
-               "64x64x64")
+SWEEP_TILES = ("256x256x64", "192x256x64", "256x192x64", "192x192x64", "256x128x64", "128x128x64_r3",
+               "128x128x64", "64x64x64_r4", "64x64x64")  # those the layout has
 
 
 def sweep(which: str = "tn") -> int:
@@ -509,9 +509,10 @@ def sweep(which: str = "tn") -> int:
         need = hgemm.gemm_ws_size(hgemm.OP_N, opB, M, N, K, dt)
         ws = torch.empty(max(need, 16) // 4, dtype=torch.float32, device="cuda")
         fn = hgemm.hgemm_tn_ex if lay == "tn" else hgemm.hgemm_nn_ex
+        names = {k["name"] for k in hgemm.kernel_table()}
         cands = {name: (lambda k=hgemm.kernel_index(name): fn(
                             M, N, K, dt, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), sp, kernel=k))
-                 for name in (f"{lay}_{dt}_{t}" for t in SWEEP_TILES)}
+                 for name in (f"{lay}_{dt}_{t}" for t in SWEEP_TILES) if name in names}
         if need > 0:  # hgemm_gemm_ws: the K split of the tail where it estimates it faster
             cands["auto with workspace"] = lambda: hgemm.hgemm_gemm_ws(
                 *args, ws.data_ptr(), need, sp)

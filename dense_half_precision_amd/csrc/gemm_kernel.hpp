@@ -174,17 +174,23 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T:
       // The LDS reads go out in batches of up to 8 before their stores, so
       // that their latencies overlap (one read, wait, store at a time took
       // 9k cycles a 256 x 256 tile), and the row pointer steps by RPI rows.
-      // A wave block inside M x N stores without per-lane predicates.
-      constexpr int LPR = T::WTN / 8, RPI = 64 / LPR;
+      // A wave block inside M x N stores without per-lane predicates.  A row
+      // of WTN = 96 (12 chunks) takes 16 lanes, the last 4 idle.
+      constexpr int CPR = T::WTN / 8;                // 16-byte chunks per row
+      constexpr int LPR = CPR > 8 ? 16 : CPR;        // lanes per row (a power of two)
+      constexpr bool FULL = LPR == CPR;              // every lane stores
+      constexpr int RPI = 64 / LPR;
       constexpr int NROW = T::WTM / RPI, BATCH = NROW < 8 ? NROW : 8;
+      static_assert((LPR & (LPR - 1)) == 0 && CPR <= LPR && 2 * CPR > LPR, "lanes per row");
       static_assert(NROW % BATCH == 0, "store batches");
-      const int row0 = lane / LPR, col = 8 * (lane % LPR);
+      const bool lane_on = FULL || (lane % LPR) < CPR;
+      const int row0 = lane / LPR, col = lane_on ? 8 * (lane % LPR) : 0;
       const char *src = cw + row0 * T::CROW + col * 2;
       uint16_t *dst = args.C + (size_t)(wm0 + row0) * ldc + (wn0 + col);
       const size_t step = (size_t)RPI * ldc;
       const bool inside = wm0 + T::WTM <= M && wn0 + T::WTN <= N;  // uniform
       const int rows_left = M - wm0 - row0;  // this lane's rows: r * RPI < rows_left
-      const bool col_in = wn0 + col < N;
+      const bool col_in = lane_on && wn0 + col < N;
 #pragma unroll
       for (int r0 = 0; r0 < NROW; r0 += BATCH) {
         u32x4 v[BATCH];
@@ -194,7 +200,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T:
         if (inside) {
 #pragma unroll
           for (int b = 0; b < BATCH; ++b) {
-            __builtin_nontemporal_store(v[b], (u32x4 *)dst);
+            if (lane_on) __builtin_nontemporal_store(v[b], (u32x4 *)dst);
             dst += step;
           }
         } else {
@@ -243,6 +249,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   constexpr int SEG_A = T::SEG_A, SEG_B = T::SEG_B;
   constexpr bool A_MN = a_mn_major(LAYOUT);  // A stored K x M: transposing reads
   constexpr bool B_MN = b_mn_major(LAYOUT);  // B stored K x N: transposing reads
+  // an m/n-contiguous operand is loaded as whole k-rows of 2*BM or 2*BN bytes
+  // per 1 KiB segment
+  static_assert(!A_MN || 1024 % (2 * BM) == 0, "m-contiguous A: 64, 128 or 256 columns");
+  static_assert(!B_MN || 1024 % (2 * BN) == 0, "n-contiguous B: 64, 128 or 256 columns");
   constexpr int NRA = A_MN ? 2 * FM : FM;    // LDS reads for the A fragments of a slice
   constexpr int NRB = B_MN ? 2 * FN : FN;    // ... and for the B fragments
   constexpr int NR = NRA + NRB;              // LDS reads per slice

@@ -125,6 +125,8 @@ using T128S5 = TileCfg<128, 128, kLdsXor, 1, 2, 2, 5, 1>;
 using T256x128 = TileCfg<256, 128>;  // 3 A + 2 B stages, 128 KiB
 using T192x256 = TileCfg<192, 256>;  // 3 A + 2 B stages, 136 KiB
 using T64R4 = TileCfg<64, 64, kLdsXor, 1, 2, 2, 4>;  // 5 A + 4 B stages, 72 KiB
+using T256x192 = TileCfg<256, 192>;  // 3 A + 2 B stages, 144 KiB
+using T192x192 = TileCfg<192, 192>;  // 3 A + 2 B stages, 120 KiB
 using T256Plain = TileCfg<256, 256, kLdsPlain>;
 using T256Direct = TileCfg<256, 256, kLdsXor, 0>;
 using R256 = RsCfg<256, 256, 2, 2, kLdsXor>;
@@ -241,6 +243,14 @@ const KernelEntry kTable[] = {
     dp_entry<T64R4, kAtTN, kBF16>("at_tn_bf16_64x64x64_r4", 4, true),
     dp_entry<T64R4, kAtNN, kF16>("at_nn_f16_64x64x64_r4", 4, true),
     dp_entry<T64R4, kAtNN, kBF16>("at_nn_bf16_64x64x64_r4", 4, true),
+    // 256 x 192 and 192 x 192 tiles (B k-contiguous: TN, and 256 x 192 with A
+    // stored transposed; 192 x 192 also needs A k-contiguous)
+    dp_entry<T256x192, kTN, kF16>("tn_f16_256x192x64", 4, true),
+    dp_entry<T256x192, kTN, kBF16>("tn_bf16_256x192x64", 4, true),
+    dp_entry<T256x192, kAtTN, kF16>("at_tn_f16_256x192x64", 4, true),
+    dp_entry<T256x192, kAtTN, kBF16>("at_tn_bf16_256x192x64", 4, true),
+    dp_entry<T192x192, kTN, kF16>("tn_f16_192x192x64", 4, true),
+    dp_entry<T192x192, kTN, kBF16>("tn_bf16_192x192x64", 4, true),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -288,6 +298,15 @@ int find_kernel(int layout, int dtype, int bm, int bn, int nsb = 2) {
 // tiles fill whole rounds (8192^3).  With it at rate 0.83 (any rate in
 // 0.78-0.92 gives the same choices) the choice is 0.3 % behind the fastest
 // kernel on average, 47 of 49 shapes within 2 %, against 2.4 % without it.
+// The 256 x 192 tile (TN, and A stored transposed) and the 192 x 192 tile
+// (TN) do the same for other shapes: 192 x 192 fills one round at 3072^2
+// (256 tiles), 1536 x 12288 and 3072 x 6144 two, 7-14 % faster than any
+// other tile there; 256 x 192 is 4-16 % faster at 6592 x 5568 and
+// 2560 x 9600.  Fitted on four measured sets of 133 shapes (tuning, check,
+// 60 drawn at random, and single rounds of 64 x 64 tiles): rates 0.83 and
+// 0.68 (flat over 0.64-0.72 for 192 x 192), with 192 x 256 at 0.80 (flat
+// over 0.78-0.82), put the choice 0.36 % behind the fastest kernel on
+// average, 124 of 133 within 2 %, against 0.83 % without the two tiles.
 constexpr int64_t kCUs = 256;
 struct TileCand {
   int bm, bn;
@@ -295,12 +314,10 @@ struct TileCand {
   double rate_shared;  // ... with more tiles than CUs
 };
 // in order of preference on equal estimates
-const TileCand kCand[5] = {{256, 256, 1.0, 1.0},
-                           {192, 256, 0.83, 0.83},
-                           {256, 128, 0.76, 0.76},
-                           {128, 128, 0.8, 0.64},
+const TileCand kCand[7] = {{256, 256, 1.0, 1.0},   {192, 256, 0.80, 0.80}, {256, 192, 0.83, 0.83},
+                           {192, 192, 0.68, 0.68}, {256, 128, 0.76, 0.76}, {128, 128, 0.8, 0.64},
                            {64, 64, 0.5, 0.37}};
-constexpr int kNumCand = 5;
+constexpr int kNumCand = 7;
 constexpr double kTileFixed = 3.0;        // prologue and epilogue of a tile, in K steps
 constexpr double kSplitFixed = 6.9;       // the fixup launch and the wait for it
 constexpr double kSlotCost = 0.055;       // one 256 KiB partial sum written and read back

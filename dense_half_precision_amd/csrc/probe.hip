@@ -585,7 +585,9 @@ hgemm_status_t hgemm_probe_operand_offsets(int mn_major, int bx, int *load_row, 
                                            int *read_off) {
   if (!load_row || !load_chunk || !read_off || (mn_major != 0 && mn_major != 1))
     return HGEMM_ERR_INVALID_ARG;
-  if (bx != 64 && bx != 128 && bx != 256) return HGEMM_ERR_INVALID_ARG;
+  // 192 rows or columns: k-contiguous only (an m/n-contiguous tile of 192
+  // has 384-byte k-rows, which do not fill whole 1 KiB load segments)
+  if (bx != 64 && bx != 128 && bx != 256 && !(bx == 192 && !mn_major)) return HGEMM_ERR_INVALID_ARG;
   const int rowb = 2 * bx;
   for (int seg = 0; seg < bx / 8; ++seg)
     for (int l = 0; l < 64; ++l) {

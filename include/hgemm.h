@@ -258,8 +258,8 @@ int hgemm_kernel_count(void);
  * "<layout>_<dtype>_<BM>x<BN>x<BK>" for the production kernels (the ones the
  * automatic choice uses: entries 0..11, 20..31, the deeper-ring "_r3"
  * entries 38..45, the 256 x 128 entries 65..72, the 192 x 256 entries
- * 73..76 (TN and NN) and the deeper-ring 64 x 64 "_r4" entries 77..84, see
- * hgemm_auto_kernel;
+ * 73..76 (TN and NN), the deeper-ring 64 x 64 "_r4" entries 77..84 and the
+ * 256 x 192 and 192 x 192 entries 85..90, see hgemm_auto_kernel;
  * "at_" layouts take A stored
  * transposed), with a suffix naming what an
  * ablation changes ("_plainlds": LDS without the XOR swizzle, "_directepi":

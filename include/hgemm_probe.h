@@ -63,7 +63,7 @@ hgemm_status_t hgemm_probe_fragments(int mn_major, int bx, const void *src, int6
 
 /*
  * Host-side: the production kernels' placement of one K step of an operand
- * tile (bx in {64, 128, 256}; XOR layout), computed by the same functions
+ * tile (bx in {64, 128, 256}, and 192 for mn_major 0; XOR layout), computed by the same functions
  * the kernels use.
  *   load_row[s*64 + l], load_chunk[s*64 + l] (bx/8 segments x 64 lanes): the
  *     tile row (mn_major 0) or k-row (mn_major 1) and the logical 16-byte
