@@ -182,8 +182,8 @@ hgemm_status_t hgemm_nn_ex(int64_t M, int64_t N, int64_t K, hgemm_dtype_t dtype,
  * that is not 16-byte aligned.
  *
  * With cfg->split == 0 (automatic; hgemm_gemm_ws) the library splits only
- * when its cost estimate says the split is faster than every unsplit tile
- * size, choosing S by the same estimate.
+ * when its cost estimate for the split is below 0.86 of the best unsplit
+ * tile's, choosing S by the same estimate.
  * hgemm_gemm_ws_size returns the workspace bytes the automatic choice would
  * use for this call (0 when it would not split; 0 for an invalid operation
  * flag, dtype or dimension <= 0).  With a workspace smaller than that (or
@@ -277,15 +277,17 @@ const char *hgemm_kernel_info(int index, int *layout, int *dtype, int *bm,
                               int *bn, int *bk);
 
 /* Kernel table index the automatic choice would use for this call (layout
- * as in hgemm_kernel_info), or -1 for invalid arguments.  The choice takes the tile
- * size (256, 128 or 64, square) with the least estimated time: rounds of
- * workgroups over the 256 CUs, times the K steps of 64 plus 3 for a tile's
- * prologue and epilogue, times the tile's area over that tile size's relative
- * throughput (1, 0.8, 0.5); ties go to the larger tile.  A single round of
+ * as in hgemm_kernel_info), or -1 for invalid arguments.  The choice takes the
+ * tile (256 x 256, 192 x 256, 256 x 192, 192 x 192, 256 x 128, 128 x 128 or
+ * 64 x 64, among those the layout has) with the least estimated time: rounds
+ * of workgroups over the 256 CUs, times the K steps of 64 plus 3 for a tile's
+ * prologue and epilogue, times the tile's area over its measured relative
+ * throughput; ties go to the earlier tile in that list.  A single round of
  * 128 x 128 tiles (at most 256) over 24 or more K steps takes that tile's
- * entry with one more LDS stage per operand (the "_r3" names).  This is the
- * choice of hgemm_tn, hgemm_nn and hgemm_gemm; hgemm_gemm_ws may split K
- * instead. */
+ * entry with one more LDS stage per operand (the "_r3" names), and a single
+ * round of 64 x 64 tiles whose A and B pass 6 MiB the entry with two more
+ * (the "_r4" names).  This is the choice of hgemm_tn, hgemm_nn and
+ * hgemm_gemm; hgemm_gemm_ws may split K instead. */
 int hgemm_auto_kernel(int layout, hgemm_dtype_t dtype, int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus
