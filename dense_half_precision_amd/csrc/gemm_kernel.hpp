@@ -120,25 +120,22 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T:
   const int wm = (unsigned)wave / T::WVN, wn = (unsigned)wave % T::WVN;
   const int wm0 = m0 + wm * T::WTM, wn0 = n0 + wn * T::WTN;
   const float alpha = args.alpha, beta = args.beta;
-  // packed output of tile (i, j) for this lane
-  auto out2 = [&](auto GEN_, int i, int j) {
+  // packed output of tile (i, j) for this lane; c: the old C there (GEN with
+  // beta != 0)
+  auto out2 = [&](auto GEN_, int i, int j, u32x2 c) {
     constexpr bool GEN = decltype(GEN_)::value;
     float x[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
     if constexpr (GEN) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] *= alpha;
       if (beta != 0.0f) {
-        const int m = wm0 + i * 16 + (lane & 15), n = wn0 + j * 16 + 4 * (lane >> 4);
-        if (m < M && n < N) {
-          const u32x2 c = *(const u32x2 *)(args.C + (size_t)m * ldc + n);
-          float c0, c1, c2, c3;
-          unpack2<DT>(c[0], c0, c1);
-          unpack2<DT>(c[1], c2, c3);
-          x[0] = __builtin_fmaf(beta, c0, x[0]);
-          x[1] = __builtin_fmaf(beta, c1, x[1]);
-          x[2] = __builtin_fmaf(beta, c2, x[2]);
-          x[3] = __builtin_fmaf(beta, c3, x[3]);
-        }
+        float c0, c1, c2, c3;
+        unpack2<DT>(c[0], c0, c1);
+        unpack2<DT>(c[1], c2, c3);
+        x[0] = __builtin_fmaf(beta, c0, x[0]);
+        x[1] = __builtin_fmaf(beta, c1, x[1]);
+        x[2] = __builtin_fmaf(beta, c2, x[2]);
+        x[3] = __builtin_fmaf(beta, c3, x[3]);
       }
     }
     u32x2 v;
@@ -146,9 +143,13 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T:
     v[1] = pack2<DT>(x[2], x[3]);
     return v;
   };
-  // In the general form the reads of the old C go one row block at a time
-  // (the empty asm keeps later rows' reads from being hoisted), so that their
-  // registers do not pile up next to the accumulators.
+  // In the general form the old C of CB row blocks of fragments is read at
+  // once (at most 128 registers a lane, free after the main loop: the operand
+  // fragments are dead by then), so that the latencies of those reads overlap;
+  // one row block at a time, they cost 8-22 % (TN f16 8192^3 to 2048^3 with
+  // beta = 1).  Elements outside M x N read as 0 and are not stored.
+  constexpr int CB = FM < 64 / FN ? FM : 64 / FN;
+  static_assert(FM % CB == 0, "row blocks of old C per batch");
   auto epilogue = [&](auto GEN_) {
     constexpr bool GEN = decltype(GEN_)::value;
     if constexpr (T::EPI) {
@@ -156,11 +157,29 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T:
       wg_barrier();                   // every wave is done with the pipeline stages
       char *cw = smem + wave * (T::WTM * T::CROW);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int i0 = 0; i0 < FM; i0 += CB) {
+        u32x2 cold[CB][FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          *(u32x2 *)(cw + (i * 16 + (lane & 15)) * T::CROW + (j * 16 + 4 * (lane >> 4)) * 2) =
-              out2(GEN_, i, j);
+        for (int i = 0; i < CB; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) cold[i][j] = u32x2{0u, 0u};
+        if (GEN && beta != 0.0f) {
+#pragma unroll
+          for (int i = 0; i < CB; ++i) {
+            const int m = wm0 + (i0 + i) * 16 + (lane & 15);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int n = wn0 + j * 16 + 4 * (lane >> 4);
+              if (m < M && n < N) cold[i][j] = *(const u32x2 *)(args.C + (size_t)m * ldc + n);
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            *(u32x2 *)(cw + ((i0 + i) * 16 + (lane & 15)) * T::CROW + (j * 16 + 4 * (lane >> 4)) * 2) =
+                out2(GEN_, i0 + i, j, cold[i][j]);
         if constexpr (GEN) asm volatile("" ::: "memory");
       }
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
@@ -220,7 +239,11 @@ __device__ __forceinline__ void store_tile(const GemmArgs &args, f32x4 (&acc)[T:
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             const int n = wn0 + j * 16 + 4 * (lane >> 4);
-            if (n < N) *(u32x2 *)(crow + n) = out2(GEN_, i, j);
+            if (n < N) {
+              u32x2 c = {0u, 0u};
+              if (GEN && beta != 0.0f) c = *(const u32x2 *)(crow + n);
+              *(u32x2 *)(crow + n) = out2(GEN_, i, j, c);
+            }
           }
         }
         if constexpr (GEN) asm volatile("" ::: "memory");
