@@ -209,6 +209,9 @@ def test_kernel_table_and_auto_choice():
     # rates: 1024^3 stays 64 x 64; 2048 x 2048 x 8192 takes one round of the
     # deeper-ring 128 x 128 kernel (28 % faster than 256 x 128)
     assert tab[hgemm.auto_kernel(0, 0, 1024, 1024, 1024)]["name"] == "tn_f16_64x64x64"
+    # four 64 x 64 workgroups sharing a CU overlap their prologues and
+    # epilogues: 468 of them beat 117 tiles of 128 x 128 (14 % measured)
+    assert tab[hgemm.auto_kernel(0, 0, 1152, 1664, 1472)]["name"] == "tn_f16_64x64x64"
     # a single round of 64 x 64 tiles whose A and B pass 6 MiB takes the ring
     # with 5 A + 4 B stages (1.5-1.8x faster measured there); under it, or with
     # more tiles than CUs, the default ring
