@@ -274,39 +274,27 @@ int find_kernel(int layout, int dtype, int bm, int bn, int nsb = 2) {
 
 // Cost model of the automatic choice, in units of one K step of a 256 x 256
 // tile on every CU at once (about 1.3 us on MI355X).  A launch of BM x BN
-// tiles runs ceil(tiles / 256 CUs) rounds of one workgroup per CU, each tile
-// taking (KT + kTileFixed) * (BM*BN / 256^2) / rate units, rate the per-CU
-// throughput of that tile relative to the 256 x 256 kernel.  The constants
-// were chosen on measured times of every tile and split over square, skinny
-// and long-K shapes.  The 128 x 128 and 64 x 64 kernels have two rates each:
-// one workgroup per CU (a single round; where the deeper-ring 128 variant
-// runs), and several sharing a CU when there are more tiles than CUs (two of
-// 128 x 128, four of 64 x 64, as their LDS allows).  Sweeps over 49 TN f16
-// and NN bf16 shapes put the shared rates at 0.58-0.70 and 0.25-0.45: with
-// the single-round rates there, the choice took the 128 tile where the 256
-// tile was 14-24 % faster (3072^3, 6000 x 6000 x 3000) and the 64 tile where
-// the 128 tile was 30 % faster (2304^3).  The 256 x 128 tile (128 KiB of LDS,
-// one workgroup per CU) covers in one round what takes the 128 tile two:
-// 6-15 % faster than the square tiles on 2304^3-2816^3, 4608^3 and
-// 1024 x 8192 x 8192 (both orientations, TN and NN).  On the same sweeps its
-// rate 0.76 brings the choice from 1.9 % to 0.4 % behind the fastest kernel
-// on average (any rate in 0.66-0.82 gives the same choices but one).  The
-// 192 x 256 tile (136 KiB, one workgroup per CU) fills the CUs where 256 x 256
-// tiles leave a partial round (3072^3: 192 tiles against 144; 6144^3: three
-// whole rounds against two and a quarter): the fastest kernel on 12 of the 49
-// sweep shapes, 3-18 % ahead of every other tile, and slower where 256 x 256
-// tiles fill whole rounds (8192^3).  With it at rate 0.83 (any rate in
-// 0.78-0.92 gives the same choices) the choice is 0.3 % behind the fastest
-// kernel on average, 47 of 49 shapes within 2 %, against 2.4 % without it.
-// The 256 x 192 tile (TN, and A stored transposed) and the 192 x 192 tile
-// (TN) do the same for other shapes: 192 x 192 fills one round at 3072^2
-// (256 tiles), 1536 x 12288 and 3072 x 6144 two, 7-14 % faster than any
-// other tile there; 256 x 192 is 4-16 % faster at 6592 x 5568 and
-// 2560 x 9600.  Fitted on four measured sets of 133 shapes (tuning, check,
-// 60 drawn at random, and single rounds of 64 x 64 tiles): rates 0.83 and
-// 0.68 (flat over 0.64-0.72 for 192 x 192), with 192 x 256 at 0.80 (flat
-// over 0.78-0.82), put the choice 0.36 % behind the fastest kernel on
-// average, 124 of 133 within 2 %, against 0.83 % without the two tiles.
+// tiles runs ceil(tiles / 256 CUs) rounds, each tile taking
+// (KT + kTileFixed) * (BM*BN / 256^2) / rate units, rate the per-CU
+// throughput of that tile relative to the 256 x 256 kernel.  The 128 x 128
+// and 64 x 64 kernels have two rates each: one workgroup per CU (a single
+// round), and several sharing a CU when there are more tiles than CUs (two of
+// 128 x 128, four of 64 x 64, as their LDS allows), which also share the
+// fixed cost.  The other tiles take one workgroup per CU.  Tiles 192 or 128
+// wide fill the CUs where square tiles leave a partial round: 256 x 128
+// covers in one round what takes the 128 tile two (1024 x 8192 x 8192: 1327
+// against 1196 TFLOPS), and 192 x 256, 256 x 192 and 192 x 192 fill rounds
+// that 256 x 256 tiles leave part empty (3072^3: 256 tiles of 192 x 192
+// against 144 of 256 x 256, 21 % faster).  The rates were fitted on measured
+// times of every production kernel over four sets of 133 shapes (square,
+// skinny, long-K, 60 drawn at random, and single rounds of 64 x 64 tiles; TN
+// f16 and NN bf16): the choice is 0.36 % behind the fastest kernel on
+// average, 124 of 133 within 2 %.  Each rate sits inside a range that gives
+// the same choices (192 x 256: 0.78-0.82; 192 x 192: 0.64-0.72; 256 x 128:
+// 0.66-0.82).  With single-round rates where CUs are shared, the choice took
+// the 128 tile where the 256 tile was 14-24 % faster (3072^3,
+// 6000 x 6000 x 3000); the shared rates, 0.64 and 0.37, were measured at
+// 0.58-0.70 and 0.25-0.45.
 constexpr int64_t kCUs = 256;
 struct TileCand {
   int bm, bn;
