@@ -14,10 +14,14 @@ from dense_half_precision_amd import build as hbuild
 
 
 @pytest.fixture(scope="module")
-def kernels(tmp_path_factory):
+def api_asm(tmp_path_factory):
     out = tmp_path_factory.mktemp("asm") / "hgemm_api.s"
-    asm = open(hbuild.asm("hgemm_api.hip", str(out))).read()
-    ks = isa_waits.kernel_bodies(asm, "_ZN5hgemm")
+    return open(hbuild.asm("hgemm_api.hip", str(out))).read()
+
+
+@pytest.fixture(scope="module")
+def kernels(api_asm):
+    ks = isa_waits.kernel_bodies(api_asm, "_ZN5hgemm")
     assert ks
     return ks
 
@@ -122,3 +126,27 @@ def test_partial_sum_stores_read_accumulators_in_place(kernels):
         dup = {r for r in src if src.count(r) > 1}
         assert not dup, f"{name}: accumulator registers stored more than once: {sorted(dup)[:4]}"
     assert checked >= 20
+
+
+def test_production_tn_nn_kernels_do_not_spill(api_asm):
+    """Every TN and NN instantiation of the production kernel template with
+    the LDS-staged epilogue (all tiles, ring depths and launch modes) keeps
+    its values in registers: no scratch.  (The register file is full in the
+    256 x 256 kernels, 256 accumulators and 256 other registers a lane, so a
+    change that raises the pressure anywhere, the epilogue included, shows
+    here as spills the main loop may pay for.)"""
+    import re
+    pat = re.compile(r"\.amdhsa_kernel (_ZN5hgemm11gemm_kernelINS_7TileCfgI((?:Li\d+E){8})EE"
+                     r"Li(\d+)ELi(\d+)ELi(\d+)E\S*)")
+    checked = 0
+    for m in pat.finditer(api_asm):
+        cfg = [int(x) for x in re.findall(r"Li(\d+)E", m.group(2))]
+        layout = int(m.group(3))
+        if cfg[3] != 1 or layout not in (0, 1):  # EPI 1, TN or NN
+            continue
+        block = api_asm[m.start():m.start() + 4000]
+        scratch = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", block).group(1))
+        assert scratch == 0, f"{m.group(1)}: {scratch} bytes of scratch"
+        checked += 1
+    assert checked >= 40
+
