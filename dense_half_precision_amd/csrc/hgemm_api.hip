@@ -733,7 +733,7 @@ const char *hgemm_status_string(hgemm_status_t status) {
 
 int hgemm_last_hip_error(void) { return g_last_hip_error; }
 
-const char *hgemm_version(void) { return "hgemm-gfx950 1.2"; }
+const char *hgemm_version(void) { return "hgemm-gfx950 1.3"; }
 
 int hgemm_kernel_count(void) { return kTableSize; }
 
