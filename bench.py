@@ -452,6 +452,14 @@ SWEEP_CHECK = ([("tn", "f16", s, s, s) for s in (2304, 2816, 3328, 3840, 4608)]
                + [("nn", "bf16", 1024, 8192, 8192), ("nn", "bf16", 6000, 6000, 3000)])
 
 
+# A fifth set: A stored transposed (at_tn: At[K][M], Bt[N][K]; at_nn: At[K][M],
+# B[K][N]).
+SWEEP_AT = ([("at_tn", "f16", s, s, s) for s in (2048, 3072, 4608, 6144, 8192)]
+            + [("at_nn", "f16", s, s, s) for s in (2048, 3072, 4608, 6144)]
+            + [("at_tn", "f16", 1024, 8192, 8192), ("at_nn", "f16", 1024, 8192, 8192),
+               ("at_nn", "bf16", 6000, 6000, 3000), ("at_tn", "bf16", 1536, 12288, 4096)])
+
+
 def sweep_wide(count: int = 60, seed: int = 20261203):
     """A third set, drawn at random and not used to set any constant: TN f16
     and NN bf16 (two to one), M and N multiples of 64 in [512, 12288], K a
@@ -486,8 +494,9 @@ def sweep(which: str = "tn") -> int:
     workspace, hgemm_gemm_ws runs the K split of the tail where its cost
     model expects a gain), the automatic choice without a workspace, and how
     far it, and the call with a workspace, fall behind the best candidate; a
-    summary line at the end.  `which`: "tn" (SWEEP_SHAPES), "check" (SWEEP_CHECK), "wide"
-    (sweep_wide()) or "small" (SWEEP_SMALL)."""
+    summary line at the end.  `which`: "tn" (SWEEP_SHAPES), "nn" (SWEEP_SHAPES as NN
+    bf16), "check" (SWEEP_CHECK), "wide" (sweep_wide()), "small" (SWEEP_SMALL) or "at"
+    (SWEEP_AT, through hgemm_gemm_ex)."""
     import numpy as np
     import torch
     from dense_half_precision_amd import hgemm
@@ -495,29 +504,38 @@ def sweep(which: str = "tn") -> int:
     hold = QueueHold()
     regrets, regrets_ws = [], []
     shapes = ([("tn", "f16", M, N, K) for M, N, K in SWEEP_SHAPES] if which == "tn"
+              else [("nn", "bf16", M, N, K) for M, N, K in SWEEP_SHAPES] if which == "nn"
               else SWEEP_CHECK if which == "check" else SWEEP_SMALL if which == "small"
-              else sweep_wide())
+              else SWEEP_AT if which == "at" else sweep_wide())
     for lay, dt, M, N, K in shapes:
         g = torch.Generator(device="cuda").manual_seed(M * 131 + N * 17 + K)
         tdt = torch.float16 if dt == "f16" else torch.bfloat16
-        dA = (torch.rand((M, K), device="cuda", generator=g) * 2 - 1).to(tdt)
-        dB = (torch.rand((N, K) if lay == "tn" else (K, N), device="cuda", generator=g) * 2 - 1).to(tdt)
+        a_t, b_t = lay.startswith("at_"), lay.endswith("tn")
+        dA = (torch.rand((K, M) if a_t else (M, K), device="cuda", generator=g) * 2 - 1).to(tdt)
+        dB = (torch.rand((N, K) if b_t else (K, N), device="cuda", generator=g) * 2 - 1).to(tdt)
         dC = torch.empty((M, N), dtype=tdt, device="cuda")
-        opB, ldb = (hgemm.OP_T, K) if lay == "tn" else (hgemm.OP_N, N)
-        args = (hgemm.OP_N, opB, M, N, K, dt, 1.0, dA.data_ptr(), K, dB.data_ptr(), ldb,
+        opA, lda = (hgemm.OP_T, M) if a_t else (hgemm.OP_N, K)
+        opB, ldb = (hgemm.OP_T, K) if b_t else (hgemm.OP_N, N)
+        args = (opA, opB, M, N, K, dt, 1.0, dA.data_ptr(), lda, dB.data_ptr(), ldb,
                 0.0, dC.data_ptr(), N)
-        need = hgemm.gemm_ws_size(hgemm.OP_N, opB, M, N, K, dt)
+        need = hgemm.gemm_ws_size(opA, opB, M, N, K, dt)
         ws = torch.empty(max(need, 16) // 4, dtype=torch.float32, device="cuda")
-        fn = hgemm.hgemm_tn_ex if lay == "tn" else hgemm.hgemm_nn_ex
+        if a_t:
+            def run(k):
+                return hgemm.hgemm_gemm(*args, sp, kernel=k)
+        else:
+            fn = hgemm.hgemm_tn_ex if lay == "tn" else hgemm.hgemm_nn_ex
+
+            def run(k):
+                return fn(M, N, K, dt, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), sp, kernel=k)
         names = {k["name"] for k in hgemm.kernel_table()}
-        cands = {name: (lambda k=hgemm.kernel_index(name): fn(
-                            M, N, K, dt, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), sp, kernel=k))
+        cands = {name: (lambda k=hgemm.kernel_index(name): run(k))
                  for name in (f"{lay}_{dt}_{t}" for t in SWEEP_TILES) if name in names}
         if need > 0:  # hgemm_gemm_ws: the K split of the tail where it estimates it faster
             cands["auto with workspace"] = lambda: hgemm.hgemm_gemm_ws(
                 *args, ws.data_ptr(), need, sp)
-        auto = hgemm.kernel_table()[hgemm.auto_kernel(hgemm.TN if lay == "tn" else hgemm.NN,
-                                                      dt, M, N, K)]["name"]
+        code = {"tn": hgemm.TN, "nn": hgemm.NN, "at_tn": hgemm.AT_TN, "at_nn": hgemm.AT_NN}[lay]
+        auto = hgemm.kernel_table()[hgemm.auto_kernel(code, dt, M, N, K)]["name"]
         flop = 2.0 * M * N * K
         n = int(min(200, max(5, 20e-3 / (flop / 1.0e15))))  # about 20 ms a run
         times = {k: [] for k in cands}
@@ -953,9 +971,10 @@ def main() -> int:
     ap.add_argument("--clock-trace", type=int, default=0, metavar="LAUNCHES",
                     help="print the engine clock over this many back-to-back launches of the "
                          "workload's kernel after 2 s idle, and exit")
-    ap.add_argument("--sweep", choices=("tn", "check", "wide", "small"), default=None,
+    ap.add_argument("--sweep", choices=("tn", "nn", "check", "wide", "small", "at"), default=None,
                     help="the automatic choice against every production kernel over a grid of "
-                         "TN f16 shapes ('tn'), a second set with NN bf16 ('check'), a seeded "
+                         "TN f16 shapes ('tn'), the same as NN bf16 ('nn'), a second set with "
+                         "NN bf16 ('check'), A stored transposed ('at'), a seeded "
                          "random third set ('wide') or single rounds of 64 x 64 tiles ('small'), "
                          "and exit")
     ap.add_argument("--phases", type=int, default=0, metavar="LAUNCHES",

@@ -82,14 +82,15 @@ __host__ __device__ __forceinline__ int chunk_pos(int r, int c) {
 // four lanes per row on two adjacent chunks; with 256 bytes of banks a 512-
 // or 256-byte row maps every row onto the same banks, so the chunk is XORed
 // with 2*(k & 3) + 8*((k >> 3) & 1): the eight rows a 32-lane half reads land
-// on distinct bank pairs.  128-byte rows already alternate between the two
-// bank halves and only need 2*((k >> 1) & 1) + 4*((k >> 3) & 1).
+// on distinct bank pairs.  128- and 384-byte rows already alternate between
+// the two bank halves and only need 2*((k >> 1) & 1) + 4*((k >> 3) & 1), a
+// value below 8 that keeps the chunk inside its 128-byte group of the row.
 template <int LDS>
 __host__ __device__ __forceinline__ int nn_chunk_xor(int k, int row_bytes) {
   if constexpr (LDS == kLdsPlain) {
     return 0;
   } else {
-    return row_bytes >= 256 ? 2 * (k & 3) + 8 * ((k >> 3) & 1)
+    return row_bytes % 256 == 0 ? 2 * (k & 3) + 8 * ((k >> 3) & 1)
                             : 2 * ((k >> 1) & 1) + 4 * ((k >> 3) & 1);
   }
 }
@@ -113,17 +114,20 @@ __host__ __device__ __forceinline__ uint32_t kmajor_load_offset(int seg, int lan
 }
 
 // M/N-contiguous operand (At[K][M], B[K][N]): k-rows of `rowb` (2 * tile
-// width) bytes; a segment holds 1024 / rowb k-rows; lane l writes k-row
-// seg*rps + l/cpr, physical chunk l%cpr, which holds logical chunk
-// (l%cpr) ^ nn_chunk_xor(k).  Chunks at or past `xdim` (the M or N edge, a
-// multiple of 8) relative to the tile origin x0 get an out-of-range offset.
+// width) bytes laid end to end; lane l of segment `seg` writes LDS byte
+// b = seg*1024 + 16*l, i.e. k-row b / rowb, physical chunk (b % rowb) / 16,
+// which holds logical chunk ((b % rowb) / 16) ^ nn_chunk_xor(k).  A 64-,
+// 128- or 256-wide tile fits whole k-rows in a segment; a 384-byte k-row
+// (192 wide) straddles segments, which changes nothing for a lane.  Chunks
+// at or past `xdim` (the M or N edge, a multiple of 8) relative to the tile
+// origin x0 get an out-of-range offset.
 template <int LDS>
 __host__ __device__ __forceinline__ uint32_t mnmajor_load_offset(int seg, int lane, int ld,
                                                                  int rowb, int x0, int xdim,
                                                                  int &chunk) {
-  const int cpr = rowb / 16, rps = 1024 / rowb;
-  const int k = seg * rps + lane / cpr;
-  const int c = (lane % cpr) ^ nn_chunk_xor<LDS>(k, rowb);
+  const unsigned b = (unsigned)(seg * 1024 + 16 * lane), rb = (unsigned)rowb;
+  const int k = (int)(b / rb);
+  const int c = (int)((b % rb) / 16u) ^ nn_chunk_xor<LDS>(k, rowb);
   chunk = c;
   return (x0 + c * 8 < xdim) ? (uint32_t)(k * ld + c * 8) * 2u : kOutOfRange;
 }

@@ -272,10 +272,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   constexpr int SEG_A = T::SEG_A, SEG_B = T::SEG_B;
   constexpr bool A_MN = a_mn_major(LAYOUT);  // A stored K x M: transposing reads
   constexpr bool B_MN = b_mn_major(LAYOUT);  // B stored K x N: transposing reads
-  // an m/n-contiguous operand is loaded as whole k-rows of 2*BM or 2*BN bytes
-  // per 1 KiB segment
-  static_assert(!A_MN || 1024 % (2 * BM) == 0, "m-contiguous A: 64, 128 or 256 columns");
-  static_assert(!B_MN || 1024 % (2 * BN) == 0, "n-contiguous B: 64, 128 or 256 columns");
+  // an m/n-contiguous operand is loaded as k-rows of 2*BM or 2*BN bytes laid
+  // end to end over the 1 KiB segments; the XOR layout covers rows of 128,
+  // 256, 384 or 512 bytes
+  static_assert(!A_MN || BM == 64 || BM == 128 || BM == 192 || BM == 256, "m-contiguous A width");
+  static_assert(!B_MN || BN == 64 || BN == 128 || BN == 192 || BN == 256, "n-contiguous B width");
   constexpr int NRA = A_MN ? 2 * FM : FM;    // LDS reads for the A fragments of a slice
   constexpr int NRB = B_MN ? 2 * FN : FN;    // ... and for the B fragments
   constexpr int NR = NRA + NRB;              // LDS reads per slice
@@ -325,10 +326,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   // k-contiguous operand (A[M][K], Bt[N][K]): segment s = 8 tile rows of 128
   // bytes; lane -> (row s*8 + lane/8, stored chunk lane%8), which holds logical
   // k-chunk (lane%8) ^ swizzle(row).
-  // m/n-contiguous operand (At[K][M], B[K][N]): segment s = RPS k-rows of
-  // 2*BX bytes; lane -> (k-row s*RPS + lane/CPR, stored chunk lane%CPR) holding
-  // m/n-chunk (lane%CPR) ^ nn_chunk_xor(k); chunks past the M/N edge (a
-  // multiple of 8) read out of range.
+  // m/n-contiguous operand (At[K][M], B[K][N]): k-rows of 2*BX bytes end to
+  // end; LDS byte b = s*1024 + 16*lane -> (k-row b / (2*BX), stored chunk
+  // (b % (2*BX)) / 16) holding m/n-chunk stored-chunk ^ nn_chunk_xor(k);
+  // chunks past the M/N edge (a multiple of 8) read out of range.
   // Wave w loads segments w*SEG .. w*SEG+SEG-1 of each operand.
   auto kmaj_off = [&](int part, int ld, int &chunk) {
     return kmajor_load_offset<T::LDS>(part, lane, ld, chunk);

@@ -227,8 +227,7 @@ const KernelEntry kTable[] = {
     dp_entry<T256x128, kAtTN, kBF16>("at_tn_bf16_256x128x64", 4, true),
     dp_entry<T256x128, kAtNN, kF16>("at_nn_f16_256x128x64", 4, true),
     dp_entry<T256x128, kAtNN, kBF16>("at_nn_bf16_256x128x64", 4, true),
-    // 192 x 256 tiles (A k-contiguous only: 192-row A tiles; the 384-byte
-    // rows of an m-contiguous A tile do not fill whole 1 KiB load segments)
+    // 192 x 256 tiles (the transposed-A forms further down)
     dp_entry<T192x256, kTN, kF16>("tn_f16_192x256x64", 4, true),
     dp_entry<T192x256, kTN, kBF16>("tn_bf16_192x256x64", 4, true),
     dp_entry<T192x256, kNN, kF16>("nn_f16_192x256x64", 4, true),
@@ -243,14 +242,29 @@ const KernelEntry kTable[] = {
     dp_entry<T64R4, kAtTN, kBF16>("at_tn_bf16_64x64x64_r4", 4, true),
     dp_entry<T64R4, kAtNN, kF16>("at_nn_f16_64x64x64_r4", 4, true),
     dp_entry<T64R4, kAtNN, kBF16>("at_nn_bf16_64x64x64_r4", 4, true),
-    // 256 x 192 and 192 x 192 tiles (B k-contiguous: TN, and 256 x 192 with A
-    // stored transposed; 192 x 192 also needs A k-contiguous)
+    // 256 x 192 and 192 x 192 tiles
     dp_entry<T256x192, kTN, kF16>("tn_f16_256x192x64", 4, true),
     dp_entry<T256x192, kTN, kBF16>("tn_bf16_256x192x64", 4, true),
     dp_entry<T256x192, kAtTN, kF16>("at_tn_f16_256x192x64", 4, true),
     dp_entry<T256x192, kAtTN, kBF16>("at_tn_bf16_256x192x64", 4, true),
     dp_entry<T192x192, kTN, kF16>("tn_f16_192x192x64", 4, true),
     dp_entry<T192x192, kTN, kBF16>("tn_bf16_192x192x64", 4, true),
+    // 192-wide m/n-contiguous operand tiles: 384-byte k-rows laid end to end
+    // over the 1 KiB load segments
+    dp_entry<T256x192, kNN, kF16>("nn_f16_256x192x64", 4, true),
+    dp_entry<T256x192, kNN, kBF16>("nn_bf16_256x192x64", 4, true),
+    dp_entry<T192x192, kNN, kF16>("nn_f16_192x192x64", 4, true),
+    dp_entry<T192x192, kNN, kBF16>("nn_bf16_192x192x64", 4, true),
+    dp_entry<T192x256, kAtTN, kF16>("at_tn_f16_192x256x64", 4, true),
+    dp_entry<T192x256, kAtTN, kBF16>("at_tn_bf16_192x256x64", 4, true),
+    dp_entry<T192x192, kAtTN, kF16>("at_tn_f16_192x192x64", 4, true),
+    dp_entry<T192x192, kAtTN, kBF16>("at_tn_bf16_192x192x64", 4, true),
+    dp_entry<T192x256, kAtNN, kF16>("at_nn_f16_192x256x64", 4, true),
+    dp_entry<T192x256, kAtNN, kBF16>("at_nn_bf16_192x256x64", 4, true),
+    dp_entry<T256x192, kAtNN, kF16>("at_nn_f16_256x192x64", 4, true),
+    dp_entry<T256x192, kAtNN, kBF16>("at_nn_bf16_256x192x64", 4, true),
+    dp_entry<T192x192, kAtNN, kF16>("at_nn_f16_192x192x64", 4, true),
+    dp_entry<T192x192, kAtNN, kBF16>("at_nn_bf16_192x192x64", 4, true),
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -733,7 +747,7 @@ const char *hgemm_status_string(hgemm_status_t status) {
 
 int hgemm_last_hip_error(void) { return g_last_hip_error; }
 
-const char *hgemm_version(void) { return "hgemm-gfx950 1.3"; }
+const char *hgemm_version(void) { return "hgemm-gfx950 1.4"; }
 
 int hgemm_kernel_count(void) { return kTableSize; }
 

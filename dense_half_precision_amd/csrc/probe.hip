@@ -562,7 +562,7 @@ hgemm_status_t hgemm_probe_fragments(int mn_major, int bx, const void *src, int6
                                      void *dst, void *stream) {
   clear_error();
   if (!src || !dst || (mn_major != 0 && mn_major != 1)) return HGEMM_ERR_INVALID_ARG;
-  if (bx != 64 && bx != 128 && bx != 256) return HGEMM_ERR_INVALID_ARG;
+  if (bx != 64 && bx != 128 && bx != 192 && bx != 256) return HGEMM_ERR_INVALID_ARG;
   if (ld < (mn_major ? bx : 64) || ld % 8 != 0 || ld > (1 << 20)) return HGEMM_ERR_INVALID_ARG;
   if (((uintptr_t)src | (uintptr_t)dst) & 15) return HGEMM_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
@@ -572,10 +572,12 @@ hgemm_status_t hgemm_probe_fragments(int mn_major, int bx, const void *src, int6
   if (mn_major) {
     if (bx == 64) hipLaunchKernelGGL((probe_fragments_kernel<1, 64>), dim3(1), dim3(64), 0, s, p, l, q);
     if (bx == 128) hipLaunchKernelGGL((probe_fragments_kernel<1, 128>), dim3(1), dim3(64), 0, s, p, l, q);
+    if (bx == 192) hipLaunchKernelGGL((probe_fragments_kernel<1, 192>), dim3(1), dim3(64), 0, s, p, l, q);
     if (bx == 256) hipLaunchKernelGGL((probe_fragments_kernel<1, 256>), dim3(1), dim3(64), 0, s, p, l, q);
   } else {
     if (bx == 64) hipLaunchKernelGGL((probe_fragments_kernel<0, 64>), dim3(1), dim3(64), 0, s, p, l, q);
     if (bx == 128) hipLaunchKernelGGL((probe_fragments_kernel<0, 128>), dim3(1), dim3(64), 0, s, p, l, q);
+    if (bx == 192) hipLaunchKernelGGL((probe_fragments_kernel<0, 192>), dim3(1), dim3(64), 0, s, p, l, q);
     if (bx == 256) hipLaunchKernelGGL((probe_fragments_kernel<0, 256>), dim3(1), dim3(64), 0, s, p, l, q);
   }
   return launched();
@@ -585,9 +587,7 @@ hgemm_status_t hgemm_probe_operand_offsets(int mn_major, int bx, int *load_row, 
                                            int *read_off) {
   if (!load_row || !load_chunk || !read_off || (mn_major != 0 && mn_major != 1))
     return HGEMM_ERR_INVALID_ARG;
-  // 192 rows or columns: k-contiguous only (an m/n-contiguous tile of 192
-  // has 384-byte k-rows, which do not fill whole 1 KiB load segments)
-  if (bx != 64 && bx != 128 && bx != 256 && !(bx == 192 && !mn_major)) return HGEMM_ERR_INVALID_ARG;
+  if (bx != 64 && bx != 128 && bx != 192 && bx != 256) return HGEMM_ERR_INVALID_ARG;
   const int rowb = 2 * bx;
   for (int seg = 0; seg < bx / 8; ++seg)
     for (int l = 0; l < 64; ++l) {

@@ -129,7 +129,7 @@ const char *hgemm_status_string(hgemm_status_t status);
 /* hipError_t of this thread's last HGEMM_ERR_HIP (0 if none yet). */
 int hgemm_last_hip_error(void);
 
-/* Library version string, e.g. "hgemm-gfx950 1.3". */
+/* Library version string, e.g. "hgemm-gfx950 1.4". */
 const char *hgemm_version(void);
 
 /*
@@ -258,8 +258,9 @@ int hgemm_kernel_count(void);
  * "<layout>_<dtype>_<BM>x<BN>x<BK>" for the production kernels (the ones the
  * automatic choice uses: entries 0..11, 20..31, the deeper-ring "_r3"
  * entries 38..45, the 256 x 128 entries 65..72, the 192 x 256 entries
- * 73..76 (TN and NN), the deeper-ring 64 x 64 "_r4" entries 77..84 and the
- * 256 x 192 and 192 x 192 entries 85..90, see hgemm_auto_kernel;
+ * 73..76 (TN and NN), the deeper-ring 64 x 64 "_r4" entries 77..84, the
+ * 256 x 192 and 192 x 192 entries 85..90 and the entries 91..104 that
+ * complete the 192-wide tiles for the other layouts, see hgemm_auto_kernel;
  * "at_" layouts take A stored
  * transposed), with a suffix naming what an
  * ablation changes ("_plainlds": LDS without the XOR swizzle, "_directepi":

@@ -51,7 +51,7 @@ hgemm_status_t hgemm_probe_mfma16(int dtype, const void *x, const void *y, float
  *               (ld >= 64);
  *   mn_major 1: src holds the same tile stored 64 x bx, element (row, k) at
  *               src[k*ld + row] (ld >= bx);
- *   bx in {64, 128, 256}; ld a multiple of 8, at most 2^20.
+ *   bx in {64, 128, 192, 256}; ld a multiple of 8, at most 2^20.
  * dst: (bx/16) x 2 x 64 entries of 16 bytes: entry [f][sl][lane] holds the 8
  *      values lane `lane` feeds the matrix core for fragment f and k-slice sl,
  *      which must be tile (16f + lane%16, 32sl + 8(lane/16) + e), e = 0..7.
@@ -63,7 +63,7 @@ hgemm_status_t hgemm_probe_fragments(int mn_major, int bx, const void *src, int6
 
 /*
  * Host-side: the production kernels' placement of one K step of an operand
- * tile (bx in {64, 128, 256}, and 192 for mn_major 0; XOR layout), computed by the same functions
+ * tile (bx in {64, 128, 192, 256}; XOR layout), computed by the same functions
  * the kernels use.
  *   load_row[s*64 + l], load_chunk[s*64 + l] (bx/8 segments x 64 lanes): the
  *     tile row (mn_major 0) or k-row (mn_major 1) and the logical 16-byte

@@ -230,19 +230,17 @@ def test_kernel_table_and_auto_choice():
     for s in (2304, 2560, 2816):
         assert tab[hgemm.auto_kernel(0, 0, s, s, s)]["name"] == "tn_f16_256x128x64", s
     # tiles of 192 rows or columns where they fill the CUs better than 256 x 256
-    # ones (3-18 % ahead of every other tile on the sweeps): 192 x 256 for NN
-    # (B n-contiguous takes no 192-column tile), 256 x 192 for TN and for A
-    # stored transposed (A m-contiguous takes no 192-row tile), 192 x 192 (TN)
-    # where it fills whole rounds (3072^2: 256 tiles)
+    # ones (3-27 % ahead of every other tile on the sweeps), in every layout:
+    # 256 x 192, and 192 x 192 where it fills whole rounds (3072^2: 256 tiles)
     for M, N, K in ((6144, 6144, 6144), (4608, 4608, 4608), (6000, 6000, 3000),
                     (7000, 5000, 4000)):
         assert tab[hgemm.auto_kernel(0, 0, M, N, K)]["name"] == "tn_f16_256x192x64", (M, N, K)
-        assert tab[hgemm.auto_kernel(1, 1, M, N, K)]["name"] == "nn_bf16_192x256x64", (M, N, K)
-    assert tab[hgemm.auto_kernel(0, 0, 3072, 3072, 3072)]["name"] == "tn_f16_192x192x64"
+        assert tab[hgemm.auto_kernel(1, 1, M, N, K)]["name"] == "nn_bf16_256x192x64", (M, N, K)
+        assert tab[hgemm.auto_kernel(3, 0, M, N, K)]["name"] == "at_nn_f16_256x192x64", (M, N, K)
+    for layout, prefix in ((0, "tn_f16"), (1, "nn_f16"), (2, "at_tn_f16"), (3, "at_nn_f16")):
+        assert tab[hgemm.auto_kernel(layout, 0, 3072, 3072, 3072)]["name"] == f"{prefix}_192x192x64"
     assert tab[hgemm.auto_kernel(0, 1, 1536, 12288, 4096)]["name"] == "tn_bf16_192x192x64"
-    assert tab[hgemm.auto_kernel(1, 1, 3072, 3072, 3072)]["name"] == "nn_bf16_192x256x64"
-    assert tab[hgemm.auto_kernel(2, 0, 3072, 3072, 3072)]["name"] == "at_tn_f16_256x192x64"
-    assert tab[hgemm.auto_kernel(3, 0, 3072, 3072, 3072)]["name"] == "at_nn_f16_256x256x64"
+    assert tab[hgemm.auto_kernel(1, 1, 1536, 12288, 4096)]["name"] == "nn_bf16_192x192x64"
     # and not where the 256 x 256 tile was faster on the same sweeps
     for s in (4096, 5120, 8192):
         assert tab[hgemm.auto_kernel(0, 0, s, s, s)]["name"] == "tn_f16_256x256x64", s

@@ -104,7 +104,8 @@ def test_every_transposed_a_kernel_ragged(kernel):
                                   "tn_f16_128x256x64", "tn_f16_256x256x64_w2x4",
                                   "tn_bf16_256x256x64_w2x4", "tn_f16_256x256x64_pp",
                                   "tn_bf16_256x256x64_pp", "tn_f16_128x128x64_ppk",
-                                  "tn_bf16_128x128x64_ppk"])
+                                  "tn_bf16_128x128x64_ppk", "nn_f16_256x192x64",
+                                  "nn_bf16_192x192x64"])
 def test_general_form_on_tn_nn_kernels(name):
     """Leading dimensions, alpha and beta through the TN/NN kernels."""
     k = hgemm.kernel_table()[hgemm.kernel_index(name)]

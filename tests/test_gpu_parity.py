@@ -129,14 +129,23 @@ def test_persistent_many_tiles(name):
 @pytest.mark.parametrize("name", ["tn_f16_192x256x64", "nn_bf16_192x256x64", "tn_f16_256x128x64",
                                   "nn_bf16_256x128x64", "at_tn_bf16_256x128x64",
                                   "at_nn_f16_256x128x64", "tn_bf16_256x192x64",
-                                  "at_tn_f16_256x192x64", "tn_f16_192x192x64"])
+                                  "at_tn_f16_256x192x64", "tn_f16_192x192x64",
+                                  # 192-wide m/n-contiguous operand tiles (384-byte k-rows)
+                                  "nn_f16_256x192x64", "nn_bf16_256x192x64",
+                                  "nn_f16_192x192x64", "nn_bf16_192x192x64",
+                                  "at_tn_f16_192x256x64", "at_tn_bf16_192x256x64",
+                                  "at_tn_f16_192x192x64", "at_tn_bf16_192x192x64",
+                                  "at_nn_f16_192x256x64", "at_nn_bf16_192x256x64",
+                                  "at_nn_f16_256x192x64", "at_nn_bf16_256x192x64",
+                                  "at_nn_f16_192x192x64", "at_nn_bf16_192x192x64"])
 def test_rectangular_tiles_at_scale(name):
     """The 192 x 256, 256 x 192, 192 x 192 and 256 x 128 production kernels
     on a few rounds of tiles with ragged last tile rows and columns (3000 =
     15 x 192 + 120 = 11 x 256 + 184; 3080 = 16 x 192 + 8) and a K tail: whole
     output by projection, a stratified sample element by element, and the same
     bits as the 256 x 256 kernel, which sums every element over the same K
-    slices in the same order."""
+    slices in the same order.  With an m- or n-contiguous operand 192 wide,
+    a 384-byte k-row straddles the 1 KiB load segments."""
     k = hgemm.kernel_table()[hgemm.kernel_index(name)]
     layout = ("tn", "nn", "at_tn", "at_nn")[k["layout"]]
     dtype = "f16" if k["dtype"] == hgemm.F16 else "bf16"

@@ -95,7 +95,7 @@ def test_mfma16_lane_map(dtype):
 
 
 @pytest.mark.parametrize("mn_major", [0, 1])
-@pytest.mark.parametrize("bx", [64, 128, 256])
+@pytest.mark.parametrize("bx", [64, 128, 192, 256])
 def test_operand_fragments(mn_major, bx):
     """One K step through the production path (direct-to-LDS placement, XOR
     layout, 16-byte or transposing fragment reads) delivers exactly the

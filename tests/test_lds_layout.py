@@ -181,7 +181,7 @@ def test_bank_conflicts(layout, worst):
 
 # ---------------------------------------------------------------- production
 @pytest.mark.parametrize("mn_major,bx", [(0, 64), (0, 128), (0, 192), (0, 256),
-                                         (1, 64), (1, 128), (1, 256)])
+                                         (1, 64), (1, 128), (1, 192), (1, 256)])
 def test_production_operand_placement(mn_major, bx):
     """The production kernels' direct-to-LDS placement and fragment reads
     (the functions the kernels use, run on the host): every chunk of the tile
