@@ -499,11 +499,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{};
-  // MFMA t of a slice: A tile i = t / FN, B tile j = t % FN (operands swapped so
-  // each lane ends with 4 consecutive columns of one row of C)
+  // MFMA t of a slice: A tile i = t / FN, B tile j = t % FN, j running backwards
+  // on odd i, so that every MFMA shares an operand with the one before it (at a
+  // change of i the B fragment, else the A fragment); operands swapped so each
+  // lane ends with 4 consecutive columns of one row of C.  Each accumulator
+  // still sums its slices in k order, so the results are the same bits; the
+  // order runs 0.4-1.4 % faster than plain row order (interleaved timing,
+  // 8192^3, NN 4096^3, 2048^3).  The persistent loop keeps the row order, with
+  // which its registers fit without scratch.
   auto mfma = [&](auto S_, int t) {
     constexpr int S = decltype(S_)::value;
-    const int i = t / FN, j = t % FN;
+    const int i = t / FN, jj = t % FN, j = (!OPAQUE && (i & 1)) ? FN - 1 - jj : jj;
     acc[i][j] = mfma16x16x32<DT>(f[S][j], f[S][FN + i], acc[i][j]);
   };
   using I0 = std::integral_constant<int, 0>;

@@ -747,7 +747,7 @@ const char *hgemm_status_string(hgemm_status_t status) {
 
 int hgemm_last_hip_error(void) { return g_last_hip_error; }
 
-const char *hgemm_version(void) { return "hgemm-gfx950 1.4"; }
+const char *hgemm_version(void) { return "hgemm-gfx950 1.5"; }
 
 int hgemm_kernel_count(void) { return kTableSize; }
 

@@ -129,7 +129,7 @@ const char *hgemm_status_string(hgemm_status_t status);
 /* hipError_t of this thread's last HGEMM_ERR_HIP (0 if none yet). */
 int hgemm_last_hip_error(void);
 
-/* Library version string, e.g. "hgemm-gfx950 1.4". */
+/* Library version string, e.g. "hgemm-gfx950 1.5". */
 const char *hgemm_version(void);
 
 /*
