@@ -504,7 +504,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &args, char *smem, int 
   // change of i the B fragment, else the A fragment); operands swapped so each
   // lane ends with 4 consecutive columns of one row of C.  Each accumulator
   // still sums its slices in k order, so the results are the same bits; the
-  // order runs 0.4-1.4 % faster than plain row order (interleaved timing,
+  // order runs 0.2-1.4 % faster than plain row order (interleaved timing,
   // 8192^3, NN 4096^3, 2048^3).  The persistent loop keeps the row order, with
   // which its registers fit without scratch.
   auto mfma = [&](auto S_, int t) {
