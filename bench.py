@@ -873,6 +873,36 @@ def phases(widx: int, launches: int, settle_ms: float) -> int:
     return 0
 
 
+def sustain(widx: int, seconds: float) -> int:
+    """The workload's automatic kernel back to back for `seconds` (a synchronisation
+    every 20 launches), for watching board power and clocks with an outside
+    tool; prints the wall-clock start and end (Unix seconds) and the rate."""
+    import numpy as np
+    import torch
+    from dense_half_precision_amd import hgemm, inputs
+    w = inputs.workload(widx)
+    A, B = inputs.operands(w)
+    dA = torch.from_numpy(A.view(np.int16)).cuda()
+    dB = torch.from_numpy(B.view(np.int16)).cuda()
+    dC = torch.empty((w.M, w.N), dtype=torch.int16, device="cuda")
+    fn = hgemm.hgemm_tn if w.layout == "tn" else hgemm.hgemm_nn
+    sp = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    t0 = time.time()
+    n = 0
+    while time.time() - t0 < seconds:
+        for _ in range(20):
+            st = fn(w.M, w.N, w.K, w.dtype, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), sp)
+            if st != hgemm.OK:
+                raise hgemm.HgemmError(st, "sustained launch")
+        n += 20
+        torch.cuda.synchronize()
+    t1 = time.time()
+    print(json.dumps({"sustain": w.name, "start_unix_s": round(t0, 3), "end_unix_s": round(t1, 3),
+                      "launches": n, "tflops": round(w.flops * n / (t1 - t0) / 1e12, 1)}), flush=True)
+    return 0
+
+
 def clock_trace(widx: int, launches: int, idle_s: float = 2.0) -> int:
     """The engine clock over a run of back-to-back launches that starts after
     `idle_s` of GPU idle time: the measurement copy of the workload's kernel
@@ -971,6 +1001,9 @@ def main() -> int:
     ap.add_argument("--clock-trace", type=int, default=0, metavar="LAUNCHES",
                     help="print the engine clock over this many back-to-back launches of the "
                          "workload's kernel after 2 s idle, and exit")
+    ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
+                    help="run the workload back to back for this many seconds (for watching "
+                         "board power and clocks with an outside tool), print the rate, and exit")
     ap.add_argument("--sweep", choices=("tn", "nn", "check", "wide", "small", "at"), default=None,
                     help="the automatic choice against every production kernel over a grid of "
                          "TN f16 shapes ('tn'), the same as NN bf16 ('nn'), a second set with "
@@ -997,6 +1030,11 @@ def main() -> int:
             print("bench.py: one GPU only", file=sys.stderr)
             return 2
         return clock_trace(args.workload, args.clock_trace)
+    if args.sustain > 0:
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            return 2
+        return sustain(args.workload, args.sustain)
     if args.sweep:
         if args.gpus != 1:
             print("bench.py: one GPU only", file=sys.stderr)
