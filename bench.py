@@ -485,7 +485,7 @@ SWEEP_TILES = ("256x256x64", "192x256x64", "256x192x64", "192x192x64", "256x128x
                "128x128x64", "64x64x64_r4", "64x64x64")  # those the layout has
 
 
-def sweep(which: str = "tn") -> int:
+def sweep(which: str = "tn", wide_seed: int = 20261203) -> int:
     """The automatic choice against every production kernel (and the K split
     of the tail, given a workspace) over SWEEP_SHAPES, TN f16, operands uniform
     in [-1, 1].  Per shape, every candidate runs back to back between one pair
@@ -495,8 +495,8 @@ def sweep(which: str = "tn") -> int:
     model expects a gain), the automatic choice without a workspace, and how
     far it, and the call with a workspace, fall behind the best candidate; a
     summary line at the end.  `which`: "tn" (SWEEP_SHAPES), "nn" (SWEEP_SHAPES as NN
-    bf16), "check" (SWEEP_CHECK), "wide" (sweep_wide()), "small" (SWEEP_SMALL) or "at"
-    (SWEEP_AT, through hgemm_gemm_ex)."""
+    bf16), "check" (SWEEP_CHECK), "wide" (sweep_wide(seed=wide_seed)), "small"
+    (SWEEP_SMALL) or "at" (SWEEP_AT, through hgemm_gemm_ex)."""
     import numpy as np
     import torch
     from dense_half_precision_amd import hgemm
@@ -506,7 +506,7 @@ def sweep(which: str = "tn") -> int:
     shapes = ([("tn", "f16", M, N, K) for M, N, K in SWEEP_SHAPES] if which == "tn"
               else [("nn", "bf16", M, N, K) for M, N, K in SWEEP_SHAPES] if which == "nn"
               else SWEEP_CHECK if which == "check" else SWEEP_SMALL if which == "small"
-              else SWEEP_AT if which == "at" else sweep_wide())
+              else SWEEP_AT if which == "at" else sweep_wide(seed=wide_seed))
     for lay, dt, M, N, K in shapes:
         g = torch.Generator(device="cuda").manual_seed(M * 131 + N * 17 + K)
         tdt = torch.float16 if dt == "f16" else torch.bfloat16
@@ -1010,6 +1010,8 @@ def main() -> int:
                          "NN bf16 ('check'), A stored transposed ('at'), a seeded "
                          "random third set ('wide') or single rounds of 64 x 64 tiles ('small'), "
                          "and exit")
+    ap.add_argument("--wide-seed", type=int, default=20261203,
+                    help="seed of the random shapes of --sweep wide")
     ap.add_argument("--phases", type=int, default=0, metavar="LAUNCHES",
                     help="after the settle phase, time the main loop's phases (wait, barrier, "
                          "rest) with the workload kernel's '_ph' copy over this many launches, "
@@ -1039,7 +1041,7 @@ def main() -> int:
         if args.gpus != 1:
             print("bench.py: one GPU only", file=sys.stderr)
             return 2
-        return sweep(args.sweep)
+        return sweep(args.sweep, args.wide_seed)
     if args.phases > 0:
         if args.gpus != 1:
             print("bench.py: one GPU only", file=sys.stderr)

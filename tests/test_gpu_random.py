@@ -20,8 +20,9 @@ pytestmark = pytest.mark.gpu
 
 NAN = {"f16": 0x7E00, "bf16": 0x7FC0}
 # 96 cases in the suite; HGEMM_RANDOM_CASES=n runs the first n of the same
-# seeded sequence (a longer campaign)
+# seeded sequence (a longer campaign), HGEMM_RANDOM_START=s from case s on
 N_CASES = int(os.environ.get("HGEMM_RANDOM_CASES", "96"))
+FIRST_CASE = int(os.environ.get("HGEMM_RANDOM_START", "0"))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -55,7 +56,7 @@ def _kernels_for(opA, opB, dt):
             and not k["name"].startswith("rs_") and not k["name"].endswith(("_clk", "_ph"))]
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
+@pytest.mark.parametrize("i", range(FIRST_CASE, FIRST_CASE + N_CASES))
 def test_random_case(i):
     c = _case(i)
     opA, opB, dt, M, N, K = c["opA"], c["opB"], c["dt"], c["M"], c["N"], c["K"]
