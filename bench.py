@@ -487,8 +487,8 @@ SWEEP_TILES = ("256x256x64", "192x256x64", "256x192x64", "192x192x64", "256x128x
 
 def sweep(which: str = "tn", wide_seed: int = 20261203) -> int:
     """The automatic choice against every production kernel (and the K split
-    of the tail, given a workspace) over SWEEP_SHAPES, TN f16, operands uniform
-    in [-1, 1].  Per shape, every candidate runs back to back between one pair
+    of the tail, given a workspace) over one set of shapes (`which`), operands
+    uniform in [-1, 1].  Per shape, every candidate runs back to back between one pair
     of events, queued behind a QueueHold launch, in three alternating rounds
     (median).  One JSON line per shape: TFLOPS of each candidate (with a
     workspace, hgemm_gemm_ws runs the K split of the tail where its cost
