@@ -307,22 +307,29 @@ int find_kernel(int layout, int dtype, int bm, int bn, int nsb = 2) {
 // the same choices (192 x 256: 0.78-0.82; 192 x 192: 0.64-0.72; 256 x 128:
 // 0.66-0.82).  With single-round rates where CUs are shared, the choice took
 // the 128 tile where the 256 tile was 14-24 % faster (3072^3,
-// 6000 x 6000 x 3000); the shared rates, 0.64 and 0.37, were measured at
-// 0.58-0.70 and 0.25-0.45.
+// 6000 x 6000 x 3000).  Where workgroups share a CU they overlap each other's
+// prologue and epilogue: four 64 x 64 tiles share the fixed cost (rate 0.37,
+// measured at 0.25-0.45); for two 128 x 128 tiles the time per round was
+// refitted on eight sets (298 shapes, two of 60 random ones measured after
+// the other constants were set) as (KT - 1) steps at rate 0.56: of 298
+// choices six change, all to faster kernels (4-18 %; NN 1152 x 7168 x 9664
+// now takes one round of 192 x 192 tiles, 4096 x 4096 x 256 the 128 tile),
+// and in leave-one-set-out fits the choice is 0.43 % behind the fastest kernel
+// on average against 0.55 % before, worst 10 % against 18 %.
 constexpr int64_t kCUs = 256;
+constexpr double kTileFixed = 3.0;        // prologue and epilogue of a tile, in K steps
 struct TileCand {
   int bm, bn;
-  double rate;         // sustained rate relative to the 256 x 256 tile
-  double rate_shared;  // ... with more tiles than CUs
-  int share;           // workgroups the LDS lets share a CU
+  double rate;          // sustained rate relative to the 256 x 256 tile
+  double rate_shared;   // ... with more tiles than CUs
+  double fixed_shared;  // fixed K steps of a tile then (workgroups sharing a CU overlap theirs)
 };
 // in order of preference on equal estimates
-const TileCand kCand[7] = {{256, 256, 1.0, 1.0, 1},   {192, 256, 0.80, 0.80, 1},
-                           {256, 192, 0.83, 0.83, 1}, {192, 192, 0.68, 0.68, 1},
-                           {256, 128, 0.76, 0.76, 1}, {128, 128, 0.8, 0.64, 2},
-                           {64, 64, 0.5, 0.37, 4}};
+const TileCand kCand[7] = {{256, 256, 1.0, 1.0, kTileFixed},   {192, 256, 0.80, 0.80, kTileFixed},
+                           {256, 192, 0.83, 0.83, kTileFixed}, {192, 192, 0.68, 0.68, kTileFixed},
+                           {256, 128, 0.76, 0.76, kTileFixed}, {128, 128, 0.8, 0.56, -1.0},
+                           {64, 64, 0.5, 0.37, kTileFixed / 4}};
 constexpr int kNumCand = 7;
-constexpr double kTileFixed = 3.0;        // prologue and epilogue of a tile, in K steps
 constexpr double kSplitFixed = 6.9;       // the fixup launch and the wait for it
 constexpr double kSlotCost = 0.055;       // one 256 KiB partial sum written and read back
 constexpr int kMaxAutoSplit = 64;
@@ -341,17 +348,17 @@ int64_t tile_count(const TileCand &c, int64_t M, int64_t N) {
 }
 
 // Workgroups that share a CU overlap each other's prologue and epilogue, so
-// there the fixed cost of a tile is divided among them (on the measured sweeps
-// this moves one choice of 133, TN 1152 x 1664 x 1472, from the 128 x 128 tile
-// to the 14 % faster 64 x 64 one).
+// there the fixed cost of a tile is smaller (for the 64 x 64 tile a quarter:
+// on the measured sweeps this moves one choice of 133, TN 1152 x 1664 x 1472,
+// from the 128 x 128 tile to the 14 % faster 64 x 64 one).  A tile costs at
+// least one step.
 double dp_cost(int i, int64_t M, int64_t N, int64_t KT) {
   const TileCand &c = kCand[i];
   const int64_t tiles = tile_count(c, M, N);
   const bool shared = tiles > kCUs;
   const double rate = shared ? c.rate_shared : c.rate;
-  const double fixed = shared ? kTileFixed / c.share : kTileFixed;
-  return (double)((tiles + kCUs - 1) / kCUs) * ((double)KT + fixed) *
-         (double)(c.bm * c.bn) / 65536.0 / rate;
+  const double steps = std::max((double)KT + (shared ? c.fixed_shared : kTileFixed), 1.0);
+  return (double)((tiles + kCUs - 1) / kCUs) * steps * (double)(c.bm * c.bn) / 65536.0 / rate;
 }
 
 // Automatic choice without a K split: the tile with the least estimated

@@ -282,7 +282,8 @@ const char *hgemm_kernel_info(int index, int *layout, int *dtype, int *bm,
  * tile (256 x 256, 192 x 256, 256 x 192, 192 x 192, 256 x 128, 128 x 128 or
  * 64 x 64, among those the layout has) with the least estimated time: rounds
  * of workgroups over the 256 CUs, times the K steps of 64 plus 3 for a tile's
- * prologue and epilogue, times the tile's area over its measured relative
+ * prologue and epilogue (fewer where 128 x 128 or 64 x 64 workgroups share a
+ * CU and overlap theirs), times the tile's area over its measured relative
  * throughput; ties go to the earlier tile in that list.  A single round of
  * 128 x 128 tiles (at most 256) over 24 or more K steps takes that tile's
  * entry with one more LDS stage per operand (the "_r3" names), and a single

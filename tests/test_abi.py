@@ -245,6 +245,17 @@ def test_kernel_table_and_auto_choice():
     for s in (4096, 5120, 8192):
         assert tab[hgemm.auto_kernel(0, 0, s, s, s)]["name"] == "tn_f16_256x256x64", s
     assert tab[hgemm.auto_kernel(0, 0, 256, 16384, 4096)]["name"] == "tn_f16_128x128x64_r3"
+    # two 128 x 128 workgroups sharing a CU: (KT - 1) steps a round at rate 0.56,
+    # which wins at a few K steps and loses to one round of 192 x 192 tiles at
+    # many (the six choices the refit moved, each to the faster kernel measured)
+    assert tab[hgemm.auto_kernel(0, 0, 4096, 4096, 256)]["name"] == "tn_f16_128x128x64"
+    assert tab[hgemm.auto_kernel(1, 1, 4096, 4096, 256)]["name"] == "nn_bf16_128x128x64"
+    assert tab[hgemm.auto_kernel(1, 1, 8000, 1280, 576)]["name"] == "nn_bf16_128x128x64"
+    assert tab[hgemm.auto_kernel(1, 1, 10688, 5248, 512)]["name"] == "nn_bf16_128x128x64"
+    assert tab[hgemm.auto_kernel(1, 1, 1344, 11584, 4416)]["name"] == "nn_bf16_192x192x64"
+    assert tab[hgemm.auto_kernel(1, 1, 1152, 7168, 9664)]["name"] == "nn_bf16_192x192x64"
+    # and K = 1024 on the same 4096^2 stays with 256 x 256 (14 % ahead there)
+    assert tab[hgemm.auto_kernel(0, 0, 4096, 4096, 1024)]["name"] == "tn_f16_256x256x64"
 
 
 @pytest.mark.parametrize("tiles_m,tiles_n", [(1, 1), (2, 2), (3, 5), (32, 32), (16, 16), (8, 8),
